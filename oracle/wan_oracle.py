@@ -1,0 +1,313 @@
+"""float64 CPU oracle for the attention sublayer of a Wan DiT block.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): used by tests, the smoke
+check and the benchmark's CPU-baseline leg, never by the product path.
+
+Sources (the pages this follows; each function names its passage):
+
+* "Wan2.2 code walkthrough" (newtid.com repost of the AUTOHUB article),
+  the WanAttentionBlock snippet (norm1 -> modulate -> self_attn -> gated
+  residual -> cross_attn(norm3(x)) -> modulated FFN), the 3D RoPE snippet
+  (frequency split ``[c - 2(c//3), c//3, c//3]``, broadcast over the (f,h,w)
+  grid, complex multiply, ``view_as_real(...).flatten``) and the
+  self-attention snippet (RoPE on q and k only, ``k_lens=seq_lens``, global
+  window, no causal mask).
+* "论文专题讲解：Wan2.1：开源视频生成系统路线" (charles2530.github.io), section
+  "Video DiT 与 Flow Matching": full spatio-temporal self-attention plus
+  cross-attention to 512 umT5 text tokens.
+* "初识wan系列模型" (huan-yin.github.io), "3D RoPE 坐标体系的建立与预计算" and
+  "Spatio-Temporal Transformer Blocks 运算流": every token gets (t, y, x)
+  coordinates and the head dimension is shared out between the three axes;
+  RoPE is a per-token complex multiply applied to Q and K.
+
+Readings taken where the pages are silent (each one is a parameter here):
+RoPE base theta = 10000; each axis gets its own standard 1D frequency ladder
+theta**(-2j/D_a) over its own D_a = 2 * (its pair count); pairs are
+interleaved (2j, 2j+1) = (re, im); positions start at 0; RMSNorm is over the
+whole H*d token row with a length-C gain unless ``per_head``; LayerNorm uses
+the population variance and no affine; softmax scale defaults to 1/sqrt(d);
+keys at or past ``k_len`` are excluded and k_len = 0 gives o = 0,
+lse = -inf.
+
+Parity status: every function below is pinned by the CPU tests
+(closed forms, invariants, library special cases, brute force). Fidelity to
+released Wan weights (theta, ladder, norm axis, eps) cannot be pinned without
+weights: those readings are "parity unpinned" against Wan itself.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Largest finite bf16: (2 - 2**-7) * 2**127.
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ----------------------------------------------------------------------------
+# bf16 <-> float64
+# ----------------------------------------------------------------------------
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64 exactly.
+
+    A bf16 value is the top half of an IEEE-754 binary32 word, so shifting the
+    16 bits up and reinterpreting as float32 is exact, as is float32->float64.
+    """
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 to the nearest bf16, ties to even; return uint16 bits.
+
+    bf16 keeps 8 significant bits (1 implicit + 7 stored) and binary32's
+    exponent range. For |x| in [2**(e-1), 2**e) the spacing of bf16 values is
+    2**(e-8) (never below the subnormal spacing 2**-133), so rounding is
+    ``rint(x / q) * q`` with q that power of two; ``np.rint`` rounds halves to
+    even and the division by a power of two is exact in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(xf / q) * q
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+    r = np.where(finite, r, x)
+    f32 = r.astype(np.float32)  # exact: at most 8 significant bits
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_round(x) -> np.ndarray:
+    """float64 -> nearest bf16 (ties to even) -> float64."""
+    return bf16_bits_to_f64(f64_to_bf16_bits(x))
+
+
+def _f64(a) -> np.ndarray:
+    """Inputs may be bf16 bit patterns (uint16) or real arrays."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# AdaLN modulation and gated residual
+# ----------------------------------------------------------------------------
+def layer_norm(r, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis without affine: (r - mean) / sqrt(var + eps).
+
+    WanAttentionBlock snippet: norm1/norm2 are LayerNorms evaluated in fp32
+    whose output is then modulated; the variance is the population variance
+    (mean of squared deviations), the plain definition of LayerNorm.
+    """
+    r = _f64(r)
+    mu = r.mean(axis=-1, keepdims=True)
+    var = ((r - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (r - mu) / np.sqrt(var + eps)
+
+
+def _per_row(v, ndim):
+    """Modulation vectors are [B, C] (one per sample, broadcast over the
+    tokens) or [B, L, C] (one per token)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v[:, None, :] if v.ndim == 2 and ndim == 3 else v
+
+
+def adaln_modulate_gate(x, y=None, gate=None, shift=None, scale=None,
+                        eps: float = 1e-6):
+    """Residual update then modulated LayerNorm of the result.
+
+    WanAttentionBlock snippet: ``x = x + y * e[2]`` (gated residual after
+    self-attention), ``x = x + cross_attn(...)`` (ungated residual after
+    cross-attention) and ``norm(x) * (1 + e[1]) + e[0]`` (AdaLN modulation with
+    scale e[1] and shift e[0]; ``(modulation + e).chunk(6)`` gives the six
+    vectors). Here:
+
+        r = x + gate * y      (y absent: r = x; gate absent: r = x + y)
+        h = LayerNorm(r) * (1 + scale) + shift   (absent scale/shift = 0)
+
+    x, y: [B, L, C]. gate/shift/scale: [B, C] or [B, L, C]. Returns (r, h).
+    """
+    x = _f64(x)
+    r = x.copy()
+    if y is not None:
+        y = _f64(y)
+        r = r + (y if gate is None else _per_row(gate, x.ndim) * y)
+    h = layer_norm(r, eps)
+    if scale is not None:
+        h = h * (1.0 + _per_row(scale, x.ndim))
+    if shift is not None:
+        h = h + _per_row(shift, x.ndim)
+    return r, h
+
+
+# ----------------------------------------------------------------------------
+# q/k RMSNorm and 3D RoPE
+# ----------------------------------------------------------------------------
+def rms_norm(x, gain, eps: float, group: int) -> np.ndarray:
+    """RMSNorm: each group of ``group`` consecutive channels is divided by
+    sqrt(mean(x**2) + eps), then multiplied by ``gain`` (length C, or None).
+
+    WanAttentionBlock / self-attention description: q and k optionally pass
+    an RMSNorm before RoPE. group = C (the whole token row) is the reading
+    taken for the block-level ``qk_norm``; group = d is the per-head variant.
+    """
+    x = _f64(x)
+    shp = x.shape
+    g = x.reshape(shp[:-1] + (shp[-1] // group, group))
+    ms = (g * g).mean(axis=-1, keepdims=True)
+    y = (g / np.sqrt(ms + eps)).reshape(shp)
+    if gain is not None:
+        y = y * np.asarray(gain, dtype=np.float64)
+    return y
+
+
+def rope3d_pair_split(d: int):
+    """Pairs per axis (t, h, w) for head size d.
+
+    3D RoPE snippet: the d/2 complex frequencies are split as
+    ``[c - 2*(c//3), c//3, c//3]`` with c = d/2 (22, 21, 21 for d = 128).
+    """
+    c = d // 2
+    return (c - 2 * (c // 3), c // 3, c // 3)
+
+
+def rope3d_token_positions(f: int, h: int, w: int) -> np.ndarray:
+    """(t, y, x) of every token of an (f, h, w) latent-patch grid, [L, 3].
+
+    Forward snippet: patches are flattened with ``flatten(2)`` over (F, H, W),
+    so the token index runs w fastest, then h, then f; the RoPE snippet expands
+    the t, h and w frequency rows over exactly that (f, h, w) order.
+    """
+    n = np.arange(f * h * w, dtype=np.int64)
+    return np.stack([n // (h * w), (n // w) % h, n % w], axis=1)
+
+
+def rope3d_angles(f: int, h: int, w: int, d: int,
+                  theta: float = 10000.0) -> np.ndarray:
+    """Rotation angle of every (token, pair), [L, d/2], float64.
+
+    Pair j belongs to axis a by the split of ``rope3d_pair_split``; with j'
+    its index inside that axis and D_a = 2 * (pairs of axis a), the angle is
+    pos_a * theta**(-2 j' / D_a). (Reading: one standard RoPE ladder per
+    axis, positions from 0; the pages give the split and the per-axis
+    broadcast, not the ladder.)
+    """
+    pos = rope3d_token_positions(f, h, w).astype(np.float64)
+    cols = []
+    for a, n_a in enumerate(rope3d_pair_split(d)):
+        omega = float(theta) ** (-(2.0 * np.arange(n_a)) / (2.0 * n_a))
+        cols.append(np.outer(pos[:, a], omega))
+    return np.concatenate(cols, axis=1)
+
+
+def rope3d_rotate(x, phi) -> np.ndarray:
+    """Rotate interleaved pairs of x [..., L, H, d] by phi [L, d/2].
+
+    3D RoPE snippet: ``x_i * freqs_i`` on the complex view of the pairs, then
+    ``view_as_real(...).flatten``: pair (2j, 2j+1) = (re, im) becomes
+    (re cos - im sin, re sin + im cos).
+    """
+    x = _f64(x)
+    phi = np.asarray(phi, dtype=np.float64)
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def qk_norm_rope3d(x, gain, grid, H: int, eps: float = 1e-6,
+                   theta: float = 10000.0, norm: bool = True,
+                   rope: bool = True, per_head: bool = False) -> np.ndarray:
+    """RMSNorm (times gain) then 3D RoPE of one projected tensor.
+
+    x: [B, L, H*d] token-major rows; grid = (f, h, w) with f*h*w = L.
+    Self-attention snippet: ``rope_apply(q)`` / ``rope_apply(k)`` after the
+    optional q/k RMSNorm; V is never rotated. With norm False the gain is not
+    applied (it belongs to the norm).
+    """
+    x = _f64(x)
+    B, L, C = x.shape
+    d = C // H
+    y = rms_norm(x, gain, eps, d if per_head else C) if norm else x.copy()
+    if rope:
+        f, hh, ww = grid
+        assert f * hh * ww == L
+        phi = rope3d_angles(f, hh, ww, d, theta)
+        y = rope3d_rotate(y.reshape(B, L, H, d), phi).reshape(B, L, C)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def attention(q, k, v, k_len: int, scale: float):
+    """Softmax attention of one (batch, head).
+
+    q: [M, d] query rows; k, v: [Lk, d]. Keys with index >= k_len do not
+    take part (``k_lens=seq_lens`` in the self-attention snippet,
+    ``context_lens`` for cross-attention); there is no causal mask (global
+    window). Returns o [M, d] and the natural-log sum-exp lse [M].
+    """
+    q = _f64(q)
+    M, d = q.shape
+    n = max(0, min(int(k_len), np.shape(k)[0]))
+    if n == 0:
+        return np.zeros((M, d)), np.full(M, -np.inf)
+    kk = _f64(k[:n])
+    vv = _f64(v[:n])
+    s = (q @ kk.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ vv) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def _mha(q, k, v, H: int, k_lens, scale, rows):
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Lq, C = q.shape
+    d = C // H
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, rows.size, C))
+    lse = np.zeros((B, H, rows.size))
+    for b in range(B):
+        kl = k.shape[1] if k_lens is None else int(k_lens[b])
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            ob, lb = attention(q[b, rows, sl], k[b, :, sl], v[b, :, sl], kl,
+                               scale)
+            o[b, :, sl] = ob
+            lse[b, h] = lb
+    return o, lse
+
+
+def self_attention(q, k, v, H: int, k_lens=None, scale=None, rows=None):
+    """Full non-causal self-attention over every video token.
+
+    Self-attention snippet: ``flash_attention(q=rope(q), k=rope(k), v,
+    k_lens=seq_lens, window_size=(-1, -1))``. q, k, v: [B, L, H*d]
+    (bf16 bits or reals); ``rows`` selects query rows (all if None).
+    Returns o [B, rows, H*d] and lse [B, H, rows].
+    """
+    return _mha(q, k, v, H, k_lens, scale, rows)
+
+
+def cross_attention(q, k, v, H: int, context_lens=None, scale=None,
+                    rows=None):
+    """Cross-attention of video queries to text keys/values.
+
+    WanAttentionBlock snippet: ``cross_attn(norm3(x), context,
+    context_lens)``; the text context is 512 umT5 tokens projected to the
+    model width. q: [B, Lq, H*d]; k, v: [B, Lk, H*d]. No RoPE.
+    """
+    return _mha(q, k, v, H, context_lens, scale, rows)

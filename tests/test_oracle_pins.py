@@ -1,0 +1,394 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle:
+closed forms, invariants, library routines for special cases, brute force on
+tiny inputs and the shapes the pages print. CPU only."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import logsumexp
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(20261203)
+
+
+# ---------------------------------------------------------------- bf16 ----
+def test_bf16_widening_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F, 0x0001],
+                    dtype=np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0,
+            (2 - 2.0 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    got = O.bf16_bits_to_f64(bits)
+    assert got.tolist() == want
+
+
+def test_bf16_rounding_ties_to_even_and_overflow():
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8),
+                  1 + 2.0 ** -8 + 2.0 ** -30, 3.5e38, 2.0 ** -134 * 3])
+    got = O.bf16_round(x)
+    assert got[0] == 1.0                      # tie -> even mantissa
+    assert got[1] == 1 + 2.0 ** -6            # tie -> even (0000010)
+    assert got[2] == -1.0
+    assert got[3] == 1 + 2.0 ** -7            # just above the tie rounds up
+    assert np.isinf(got[4])
+    assert got[5] == 2.0 ** -132              # subnormal: 1.5 quanta -> 2 (even)
+
+
+def test_bf16_rounding_matches_torch_for_fp32_values():
+    # torch's float32 -> bfloat16 conversion rounds to nearest even; for values
+    # that are exactly float32 the float64 route must agree bit for bit.
+    x32 = (RNG.standard_normal(200000) * np.exp(RNG.uniform(-20, 20, 200000))
+           ).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy()
+    got = O.f64_to_bf16_bits(x32.astype(np.float64))
+    assert np.array_equal(got, want.view(np.uint16))
+
+
+# ----------------------------------------------------------- LayerNorm ----
+def test_layer_norm_closed_form():
+    # r = [1,2,3,4]: mean 2.5, population variance 1.25.
+    r = np.array([[1.0, 2.0, 3.0, 4.0]])
+    want = (r - 2.5) / math.sqrt(1.25 + 1e-6)
+    assert np.allclose(O.layer_norm(r, 1e-6), want, atol=1e-15)
+
+
+def test_layer_norm_matches_torch():
+    x = RNG.standard_normal((3, 7, 96)) * 3 + 1
+    want = F.layer_norm(torch.from_numpy(x), (96,), eps=1e-6).numpy()
+    assert np.allclose(O.layer_norm(x, 1e-6), want, atol=1e-12)
+
+
+def test_layer_norm_moments():
+    x = RNG.standard_normal((5, 256)) * 0.01
+    n = O.layer_norm(x, 1e-6)
+    var = x.var(axis=1)
+    assert np.allclose(n.mean(axis=1), 0, atol=1e-12)
+    assert np.allclose((n ** 2).mean(axis=1), var / (var + 1e-6), atol=1e-12)
+
+
+# ---------------------------------------------------------------- AdaLN ----
+def test_adaln_closed_form_gate_scale_shift():
+    # x = 0, y = [1,2,3,4], gate = 2 -> r = [2,4,6,8]: mean 5, var 5;
+    # LN(r) = [-3,-1,1,3]/sqrt(5); scale = 1 doubles it; shift adds 0.5.
+    x = np.zeros((1, 1, 4))
+    y = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    gate = np.full((1, 4), 2.0)
+    scale = np.full((1, 4), 1.0)
+    shift = np.full((1, 4), 0.5)
+    r, h = O.adaln_modulate_gate(x, y, gate, shift, scale, eps=0.0)
+    assert np.allclose(r, [[[2, 4, 6, 8]]])
+    want = np.array([-3, -1, 1, 3]) / math.sqrt(5) * 2 + 0.5
+    assert np.allclose(h[0, 0], want, atol=1e-14)
+
+
+def test_adaln_special_cases():
+    B, L, C = 2, 5, 64
+    x = RNG.standard_normal((B, L, C))
+    y = RNG.standard_normal((B, L, C))
+    zero = np.zeros((B, C))
+    r, h = O.adaln_modulate_gate(x, y, zero, zero, zero)
+    assert np.array_equal(r, x)                       # gate 0 -> x' = x
+    assert np.allclose(h, O.layer_norm(x, 1e-6))      # scale=shift=0 -> LN
+    r2, _ = O.adaln_modulate_gate(x, None)
+    assert np.array_equal(r2, x)                      # no y -> x' = x
+    r3, _ = O.adaln_modulate_gate(x, y)               # no gate -> x + y
+    assert np.allclose(r3, x + y)
+
+
+def test_adaln_per_sample_equals_repeated_per_token():
+    B, L, C = 2, 6, 32
+    x, y = RNG.standard_normal((2, B, L, C))
+    g, sh, sc = RNG.standard_normal((3, B, C))
+    r1, h1 = O.adaln_modulate_gate(x, y, g, sh, sc)
+    rep = lambda v: np.repeat(v[:, None, :], L, axis=1)
+    r2, h2 = O.adaln_modulate_gate(x, y, rep(g), rep(sh), rep(sc))
+    assert np.allclose(r1, r2) and np.allclose(h1, h2)
+    # batches are independent: sample 1 uses sample 1's vectors
+    _, h3 = O.adaln_modulate_gate(x[1:], y[1:], g[1:], sh[1:], sc[1:])
+    assert np.allclose(h1[1:], h3)
+
+
+# -------------------------------------------------------------- RMSNorm ----
+def test_rms_norm_closed_form():
+    x = np.array([[3.0, 4.0]])
+    y = O.rms_norm(x, np.array([2.0, 0.5]), 0.0, 2)
+    rms = math.sqrt(12.5)
+    assert np.allclose(y, [[2 * 3 / rms, 0.5 * 4 / rms]], atol=1e-15)
+
+
+def test_rms_norm_matches_torch_and_invariants():
+    x = RNG.standard_normal((4, 9, 256)) * 2.5
+    g = 1 + 0.1 * RNG.standard_normal(256)
+    want = F.rms_norm(torch.from_numpy(x), (256,), torch.from_numpy(g),
+                      eps=1e-6).numpy()
+    assert np.allclose(O.rms_norm(x, g, 1e-6, 256), want, atol=1e-12)
+    y = O.rms_norm(x, None, 1e-6, 256)
+    m = (x ** 2).mean(axis=-1)
+    assert np.allclose((y ** 2).mean(axis=-1), m / (m + 1e-6), atol=1e-12)
+    assert np.allclose(O.rms_norm(7.0 * x, None, 0.0, 256),
+                       O.rms_norm(x, None, 0.0, 256), atol=1e-12)
+
+
+def test_rms_norm_per_head_groups():
+    x = RNG.standard_normal((2, 3, 4 * 32))
+    y = O.rms_norm(x, None, 1e-6, 32)
+    for h in range(4):
+        sl = slice(32 * h, 32 * h + 32)
+        want = F.rms_norm(torch.from_numpy(x[..., sl]), (32,), eps=1e-6).numpy()
+        assert np.allclose(y[..., sl], want, atol=1e-12)
+
+
+# ----------------------------------------------------------------- RoPE ----
+def test_rope_split_d128():
+    # c = 64: [64 - 2*21, 21, 21]
+    assert O.rope3d_pair_split(128) == (22, 21, 21)
+    assert sum(O.rope3d_pair_split(128)) == 64
+
+
+def test_token_order_brute_force():
+    f, h, w = 3, 4, 5
+    pos = O.rope3d_token_positions(f, h, w)
+    n = 0
+    for t in range(f):
+        for y in range(h):
+            for x in range(w):
+                assert tuple(pos[n]) == (t, y, x)
+                n += 1
+    assert n == len(pos)
+
+
+def test_token_grids_printed_on_pages():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "wan_token_grids.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert rows
+    for frames, lf, lh, lw, ph, pw, tokens, _src in rows:
+        f, h, w = int(lf), int(lh) // int(ph), int(lw) // int(pw)
+        assert 1 + (int(frames) - 1) // 4 == f     # 4x causal time stride
+        pos = O.rope3d_token_positions(f, h, w)
+        assert len(pos) == int(tokens)
+        assert tuple(pos[-1]) == (f - 1, h - 1, w - 1)
+
+
+def test_rope_closed_form_angles():
+    f, h, w, d, th = 4, 6, 7, 128, 10000.0
+    phi = O.rope3d_angles(f, h, w, d, th)
+    n = 3 * h * w + 5 * w + 6        # token (t, y, x) = (3, 5, 6)
+    assert phi[n, 0] == 3.0 and phi[n, 22] == 5.0 and phi[n, 43] == 6.0
+    assert math.isclose(phi[n, 21], 3 * th ** (-42 / 44), rel_tol=1e-14)
+    assert math.isclose(phi[n, 42], 5 * th ** (-40 / 42), rel_tol=1e-14)
+    assert math.isclose(phi[n, 63], 6 * th ** (-40 / 42), rel_tol=1e-14)
+    assert math.isclose(phi[n, 1], 3 * th ** (-2 / 44), rel_tol=1e-14)
+    assert math.isclose(phi[n, 44], 6 * th ** (-2 / 42), rel_tol=1e-14)
+    assert np.all(phi[0] == 0)
+
+
+def _rope(x, grid, d=128, theta=10000.0):
+    f, h, w = grid
+    return O.rope3d_rotate(x, O.rope3d_angles(f, h, w, d, theta))
+
+
+def test_rope_identity_at_origin_and_pair_norms():
+    grid = (2, 3, 4)
+    x = RNG.standard_normal((24, 2, 128))
+    y = _rope(x, grid)
+    assert np.array_equal(y[0], x[0])
+    nx = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    ny = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.allclose(nx, ny, rtol=1e-13)
+
+
+def test_rope_is_complex_multiply():
+    grid = (3, 2, 5)
+    x = RNG.standard_normal((30, 3, 128))
+    phi = O.rope3d_angles(*grid, 128)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * phi)[:, None, :]
+    y = O.rope3d_rotate(x, phi)
+    assert np.allclose(y[..., 0::2], z.real, atol=1e-13)
+    assert np.allclose(y[..., 1::2], z.imag, atol=1e-13)
+
+
+def _roformer_1d(vec, m, theta=10000.0):
+    """Textbook 1D RoPE (RoFormer): block-diagonal 2x2 rotations with
+    angles m * theta**(-2(i-1)/D), i = 1..D/2, as an explicit matrix."""
+    D = vec.shape[-1]
+    R = np.zeros((D, D))
+    for i in range(D // 2):
+        a = m * theta ** (-2.0 * i / D)
+        R[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[math.cos(a), -math.sin(a)],
+                                               [math.sin(a), math.cos(a)]]
+    return R @ vec
+
+
+def test_rope_each_axis_is_textbook_1d_rope():
+    f, h, w = 5, 6, 7
+    x = RNG.standard_normal((f * h * w, 1, 128))
+    y = _rope(x, (f, h, w))
+    for (t, yy, xx) in [(4, 0, 0), (0, 5, 0), (0, 0, 6), (3, 2, 1)]:
+        n = t * h * w + yy * w + xx
+        assert np.allclose(y[n, 0, 0:44], _roformer_1d(x[n, 0, 0:44], t))
+        assert np.allclose(y[n, 0, 44:86], _roformer_1d(x[n, 0, 44:86], yy))
+        assert np.allclose(y[n, 0, 86:128], _roformer_1d(x[n, 0, 86:128], xx))
+
+
+def test_rope_scores_depend_only_on_offset():
+    f, h, w = 6, 7, 8
+    grid = (f, h, w)
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal(128)
+    X = np.zeros((f * h * w, 1, 128))
+    X[:] = q
+    Rq = _rope(X, grid)[:, 0]
+    X[:] = k
+    Rk = _rope(X, grid)[:, 0]
+    idx = lambda t, y, x: t * h * w + y * w + x
+    p, pp = (1, 2, 3), (3, 1, 0)
+    base = Rq[idx(*p)] @ Rk[idx(*pp)]
+    for delta in [(1, 0, 0), (0, 2, 0), (0, 0, 4), (2, 3, 1)]:
+        a = tuple(u + dd for u, dd in zip(p, delta))
+        b = tuple(u + dd for u, dd in zip(pp, delta))
+        assert math.isclose(Rq[idx(*a)] @ Rk[idx(*b)], base, rel_tol=1e-10,
+                            abs_tol=1e-10)
+    # and it does change with the offset
+    assert not math.isclose(Rq[idx(1, 2, 4)] @ Rk[idx(*pp)], base,
+                            rel_tol=1e-6)
+
+
+def test_rope_axis_separation():
+    # tokens that differ only in x leave the t and h pairs unchanged
+    f, h, w = 2, 3, 9
+    x = RNG.standard_normal((1, 128))
+    X = np.repeat(x[None], f * h * w, axis=0)
+    Y = _rope(X, (f, h, w))
+    a, b = 1 * h * w + 2 * w + 0, 1 * h * w + 2 * w + 8
+    assert np.allclose(Y[a, 0, :86], Y[b, 0, :86])
+    assert not np.allclose(Y[a, 0, 86:], Y[b, 0, 86:])
+
+
+def test_norm_and_rope_commute_with_unit_gain():
+    B, f, h, w, H = 1, 2, 3, 4, 3
+    L, C = f * h * w, H * 128
+    x = RNG.standard_normal((B, L, C))
+    a = O.qk_norm_rope3d(x, None, (f, h, w), H)
+    rot = _rope(x.reshape(B, L, H, 128)[0], (f, h, w)).reshape(B, L, C)
+    b = O.rms_norm(rot, None, 1e-6, C)
+    assert np.allclose(a, b, atol=1e-12)
+    m = (x ** 2).mean(-1)
+    assert np.allclose((a ** 2).mean(-1), m / (m + 1e-6), atol=1e-12)
+
+
+# ------------------------------------------------------------ attention ----
+def _sdpa64(q, k, v, scale):
+    return F.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None], torch.from_numpy(k)[None, None],
+        torch.from_numpy(v)[None, None], scale=scale).numpy()[0, 0]
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    q, k, v = RNG.standard_normal((3, 37, 64)) * 2
+    o, lse = O.attention(q, k, v, 37, 0.125)
+    assert np.allclose(o, _sdpa64(q, k, v, 0.125), atol=1e-12)
+    assert np.allclose(lse, logsumexp(q @ k.T * 0.125, axis=1), atol=1e-12)
+
+
+def test_attention_brute_force_scalar_loops():
+    M, N, d = 3, 5, 4
+    q = RNG.standard_normal((M, d))
+    k = RNG.standard_normal((N, d))
+    v = RNG.standard_normal((N, d))
+    scale = 0.7
+    o, _ = O.attention(q, k, v, N, scale)
+    for i in range(M):
+        w = []
+        for j in range(N):
+            s = 0.0
+            for c in range(d):
+                s += q[i, c] * k[j, c]
+            w.append(math.exp(s * scale))
+        tot = sum(w)
+        for c in range(d):
+            acc = 0.0
+            for j in range(N):
+                acc += w[j] * v[j, c]
+            assert math.isclose(o[i, c], acc / tot, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_attention_invariants():
+    M, N, d = 16, 40, 32
+    q = RNG.standard_normal((M, d)) * 3
+    k = RNG.standard_normal((N, d))
+    v = RNG.standard_normal((N, d))
+    s = 1 / math.sqrt(d)
+    o1, _ = O.attention(q, k, np.ones((N, d)), N, s)
+    assert np.allclose(o1, 1.0, atol=1e-13)                   # rows sum to 1
+    c = RNG.standard_normal(d)
+    oc, _ = O.attention(q, k, np.tile(c, (N, 1)), N, s)
+    assert np.allclose(oc, c, atol=1e-13)                     # constant V
+    oz, _ = O.attention(np.zeros((M, d)), k, v, 25, s)
+    assert np.allclose(oz, v[:25].mean(axis=0), atol=1e-13)   # q=0 -> mean
+    perm = RNG.permutation(N)
+    o, _ = O.attention(q, k, v, N, s)
+    op, _ = O.attention(q, k[perm], v[perm], N, s)
+    assert np.allclose(o, op, atol=1e-12)                     # no hidden order
+    k2, v2 = k.copy(), v.copy()
+    k2[30:] = 100 * RNG.standard_normal((10, d))
+    v2[30:] = 1e3
+    oa, la = O.attention(q, k, v, 30, s)
+    ob, lb = O.attention(q, k2, v2, 30, s)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)  # mask
+    o0, l0 = O.attention(q, k, v, 0, s)
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))       # empty
+    kp = k.copy()
+    kp[7] = q[3] * 50                                          # peaked key
+    opk, _ = O.attention(q[3:4], kp, v, N, 1.0)
+    assert np.allclose(opk[0], v[7], atol=1e-10)
+
+
+def test_multihead_rows_batches_and_heads():
+    B, L, H, d = 2, 23, 3, 16
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    kl = np.array([23, 11])
+    o, lse = O.self_attention(q, k, v, H, kl, None)
+    for b in range(B):
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            want = _sdpa64(q[b, :, sl], k[b, :kl[b], sl], v[b, :kl[b], sl],
+                           1 / math.sqrt(d))
+            assert np.allclose(o[b, :, sl], want, atol=1e-12)
+    rows = np.array([0, 5, 22])
+    o2, l2 = O.self_attention(q, k, v, H, kl, None, rows=rows)
+    assert np.array_equal(o2, o[:, rows]) and np.array_equal(l2, lse[:, :, rows])
+    # cross-attention: separate key length, mask per batch
+    kt, vt = RNG.standard_normal((2, B, 9, H * d))
+    oc, _ = O.cross_attention(q, kt, vt, H, np.array([9, 4]))
+    want = _sdpa64(q[1, :, :d], kt[1, :4, :d], vt[1, :4, :d], 1 / math.sqrt(d))
+    assert np.allclose(oc[1, :, :d], want, atol=1e-12)
+
+
+def test_oracle_bf16_bits_inputs():
+    x = RNG.standard_normal((1, 4, 256)).astype(np.float32)
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wid = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.bf16_bits_to_f64(bits), wid)
+    assert np.allclose(O.rms_norm(bits, None, 1e-6, 256),
+                       O.rms_norm(wid, None, 1e-6, 256))
+
+
+def test_oracle_is_independent_of_the_library():
+    import ast
+    src_dir = os.path.join(os.path.dirname(GOLDEN), "..", "oracle")
+    for name in os.listdir(src_dir):
+        if name.endswith(".py"):
+            tree = ast.parse(open(os.path.join(src_dir, name)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, (ast.Import, ast.ImportFrom)):
+                    mods = [a.name for a in node.names] if isinstance(node, ast.Import) \
+                        else [node.module or ""]
+                    for m in mods:
+                        assert not m.startswith("attention_wan_qk_amd"), name
+                        assert m.split(".")[0] in ("numpy", "__future__", "") or \
+                            m.startswith("wan_oracle"), (name, m)
