@@ -1,0 +1,293 @@
+// C ABI of libwanattn: host-side argument checks, then one kernel launch per
+// call. Nothing is enqueued unless every check passes.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/wanattn.h"
+#include "wan_internal.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxC = 8192;
+constexpr int kMaxGrid = 1024;  // length of the precomputed RoPE table on the pages
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) touched by a token-major tensor.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range span_bf16(const void* p, int64_t rows, int64_t ld, int64_t width) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + (uintptr_t)(((rows - 1) * ld + width) * 2)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Outputs may be exactly an input (in place, same stride); any other overlap
+// is rejected.
+bool bad_alias(const void* out, Range ro, int64_t ld_out, const void* in, Range ri,
+               int64_t ld_in) {
+  if (!out || !in) return false;
+  if (out == in) return ld_out != ld_in;
+  return overlap(ro, ri);
+}
+
+// Two token-major tensors of `rows` rows and C columns either touch disjoint
+// byte ranges, or are column slices of the same rows (same stride, start
+// offsets at least C apart and both inside one row).
+bool slices_disjoint(const void* a, int64_t ld_a, const void* b, int64_t ld_b, int64_t rows,
+                     int64_t C) {
+  if (!overlap(span_bf16(a, rows, ld_a, C), span_bf16(b, rows, ld_b, C))) return true;
+  if (ld_a != ld_b) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t d = pa > pb ? pa - pb : pb - pa;
+  return d >= (uintptr_t)(2 * C) && d <= (uintptr_t)(2 * (ld_a - C));
+}
+
+wanStatus_t from_hip(hipError_t e) {
+  return e == hipSuccess ? WAN_SUCCESS : WAN_ERROR_LAUNCH;
+}
+
+// Shared checks of the two attention calls.
+wanStatus_t check_attn(void* o, const float* lse, const void* q, const void* k,
+                       const void* v, int B, int Lq, int Lk, int H, int D,
+                       int64_t& ld_q, int64_t& ld_k, int64_t& ld_v, int64_t& ld_o,
+                       float softmax_scale) {
+  if (B < 0 || Lq < 0 || Lk < 1 || H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+  if (D != kHeadDim) return WAN_ERROR_NOT_SUPPORTED;
+  if (!o || !q || !k || !v) return WAN_ERROR_INVALID_VALUE;
+  if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return WAN_ERROR_INVALID_VALUE;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t C = (int64_t)H * D;
+  if (C > (int64_t)1 << 24) return WAN_ERROR_NOT_SUPPORTED;
+  int64_t* lds[4] = {&ld_q, &ld_k, &ld_v, &ld_o};
+  for (int64_t* ld : lds) {
+    if (*ld == 0) *ld = C;
+    if (*ld < C || (*ld & 7)) return WAN_ERROR_INVALID_VALUE;
+  }
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t rq = (int64_t)B * Lq, rk = (int64_t)B * Lk;
+  const Range ro = span_bf16(o, rq, ld_o, C);
+  if (overlap(ro, span_bf16(q, rq, ld_q, C)) || overlap(ro, span_bf16(k, rk, ld_k, C)) ||
+      overlap(ro, span_bf16(v, rk, ld_v, C)))
+    return WAN_ERROR_INVALID_VALUE;
+  if (lse) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(lse);
+    const Range rl{lo, lo + (uintptr_t)((int64_t)B * H * Lq * 4)};
+    if (overlap(rl, ro) || overlap(rl, span_bf16(q, rq, ld_q, C)) ||
+        overlap(rl, span_bf16(k, rk, ld_k, C)) || overlap(rl, span_bf16(v, rk, ld_v, C)))
+      return WAN_ERROR_INVALID_VALUE;
+  }
+  if ((int64_t)B * H * ((Lq + 127) / 128) > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
+  return WAN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wan_status_string(wanStatus_t status) {
+  switch (status) {
+    case WAN_SUCCESS: return "WAN_SUCCESS";
+    case WAN_ERROR_INVALID_VALUE: return "WAN_ERROR_INVALID_VALUE";
+    case WAN_ERROR_NOT_SUPPORTED: return "WAN_ERROR_NOT_SUPPORTED";
+    case WAN_ERROR_LAUNCH: return "WAN_ERROR_LAUNCH";
+  }
+  return "WAN_ERROR_UNKNOWN";
+}
+
+int wan_version(void) { return 100; }  // 0.1.0
+
+wanStatus_t wan_qk_norm_rope3d(void* q_out, void* k_out, const void* q, const void* k,
+                               const float* gain_q, const float* gain_k, int B, int L,
+                               int H, int D, int grid_f, int grid_h, int grid_w,
+                               int64_t ld_in, int64_t ld_out, float eps, float rope_theta,
+                               unsigned flags, hipStream_t stream) {
+  if (B < 0 || L < 0 || H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+  if (D != kHeadDim) return WAN_ERROR_NOT_SUPPORTED;
+  const int64_t C = (int64_t)H * D;
+  if (C > kMaxC) return WAN_ERROR_NOT_SUPPORTED;
+  if (flags & ~(WAN_NORM | WAN_ROPE | WAN_NORM_PER_HEAD)) return WAN_ERROR_INVALID_VALUE;
+  if ((flags & WAN_NORM_PER_HEAD) && !(flags & WAN_NORM)) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * L == 0) return WAN_SUCCESS;
+  if (!q && !k) return WAN_ERROR_INVALID_VALUE;
+  if ((q == nullptr) != (q_out == nullptr) || (k == nullptr) != (k_out == nullptr))
+    return WAN_ERROR_INVALID_VALUE;
+  const void* ptrs[4] = {q_out, k_out, q, k};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return WAN_ERROR_INVALID_VALUE;
+  if ((gain_q && !aligned16(gain_q)) || (gain_k && !aligned16(gain_k)))
+    return WAN_ERROR_INVALID_VALUE;
+  if (ld_in == 0) ld_in = C;
+  if (ld_out == 0) ld_out = C;
+  if (ld_in < C || ld_out < C || (ld_in & 7) || (ld_out & 7)) return WAN_ERROR_INVALID_VALUE;
+  if (!(eps >= 0.f) || isinf(eps)) return WAN_ERROR_INVALID_VALUE;
+  if (flags & WAN_ROPE) {
+    if (grid_f < 1 || grid_h < 1 || grid_w < 1 || grid_f > kMaxGrid || grid_h > kMaxGrid ||
+        grid_w > kMaxGrid)
+      return WAN_ERROR_INVALID_VALUE;
+    if ((int64_t)grid_f * grid_h * grid_w != L) return WAN_ERROR_INVALID_VALUE;
+    if (!(rope_theta > 1.f) || isinf(rope_theta)) return WAN_ERROR_INVALID_VALUE;
+  }
+  const int64_t rows = (int64_t)B * L;
+  if (rows / 4 + 1 > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
+  // Outputs may equal their own input (in place, same stride). Otherwise an
+  // output may share bytes with another tensor only as a disjoint column
+  // slice of the same rows (q/k slices of one fused projection buffer).
+  struct T {
+    const void* p;
+    int64_t ld;
+  };
+  const T outs[2] = {{q_out, ld_out}, {k_out, ld_out}};
+  const T ins[2] = {{q, ld_in}, {k, ld_in}};
+  if (q_out && k_out && !slices_disjoint(q_out, ld_out, k_out, ld_out, rows, C))
+    return WAN_ERROR_INVALID_VALUE;
+  for (int i = 0; i < 2; ++i) {
+    if (!outs[i].p) continue;
+    for (int j = 0; j < 2; ++j) {
+      if (!ins[j].p) continue;
+      if (i == j && outs[i].p == ins[j].p) {
+        if (outs[i].ld != ins[j].ld) return WAN_ERROR_INVALID_VALUE;
+        continue;
+      }
+      if (!slices_disjoint(outs[i].p, outs[i].ld, ins[j].p, ins[j].ld, rows, C))
+        return WAN_ERROR_INVALID_VALUE;
+    }
+  }
+
+  wan::NormRopeArgs a;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.q = q;
+  a.k = k;
+  a.gain_q = gain_q;
+  a.gain_k = gain_k;
+  a.rows = rows;
+  a.L = L;
+  a.H = H;
+  a.D = D;
+  a.grid_f = grid_f;
+  a.grid_h = grid_h;
+  a.grid_w = grid_w;
+  a.ld_in = ld_in;
+  a.ld_out = ld_out;
+  a.eps = eps;
+  a.log2_theta = (flags & WAN_ROPE) ? log2f(rope_theta) : 0.f;
+  a.flags = flags;
+  return from_hip(wan::launch_norm_rope(a, stream));
+}
+
+wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k, const void* v,
+                              const int32_t* k_lens, int B, int L, int H, int D, int64_t ld_q,
+                              int64_t ld_k, int64_t ld_v, int64_t ld_o, float softmax_scale,
+                              hipStream_t stream) {
+  if (B < 0 || L < 0) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * L == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  wanStatus_t st = check_attn(o, lse, q, k, v, B, L, L, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  wan::AttnArgs a;
+  a.o = o;
+  a.lse = lse;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_lens = k_lens;
+  a.B = B;
+  a.Lq = L;
+  a.Lk = L;
+  a.H = H;
+  a.ld_q = ld_q;
+  a.ld_k = ld_k;
+  a.ld_v = ld_v;
+  a.ld_o = ld_o;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return from_hip(wan::launch_attn_fwd(a, stream));
+}
+
+wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void* v,
+                               const int32_t* context_lens, int B, int Lq, int Lk, int H, int D,
+                               int64_t ld_q, int64_t ld_kv, int64_t ld_o, float softmax_scale,
+                               hipStream_t stream) {
+  if (B < 0 || Lq < 0 || Lk < 1) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * Lq == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  int64_t ld_k = ld_kv, ld_v = ld_kv;
+  wanStatus_t st = check_attn(o, nullptr, q, k, v, B, Lq, Lk, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  wan::AttnArgs a;
+  a.o = o;
+  a.lse = nullptr;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_lens = context_lens;
+  a.B = B;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.H = H;
+  a.ld_q = ld_q;
+  a.ld_k = ld_k;
+  a.ld_v = ld_v;
+  a.ld_o = ld_o;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return from_hip(wan::launch_attn_fwd(a, stream));
+}
+
+wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x, const void* y,
+                                    const float* gate, const float* shift, const float* scale,
+                                    int B, int L, int C, int64_t mod_stride_b,
+                                    int64_t mod_stride_l, float eps, hipStream_t stream) {
+  if (B < 0 || L < 0 || C < 1) return WAN_ERROR_INVALID_VALUE;
+  if (C & 7) return WAN_ERROR_INVALID_VALUE;
+  if (C > kMaxC) return WAN_ERROR_NOT_SUPPORTED;
+  if ((int64_t)B * L == 0) return WAN_SUCCESS;
+  if (!x || (!x_out && !h_out)) return WAN_ERROR_INVALID_VALUE;
+  const void* ptrs[7] = {x_out, h_out, x, y, gate, shift, scale};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return WAN_ERROR_INVALID_VALUE;
+  if (mod_stride_b == 0) mod_stride_b = C;
+  if (mod_stride_b < 0 || mod_stride_l < 0 || (mod_stride_b & 3) || (mod_stride_l & 3))
+    return WAN_ERROR_INVALID_VALUE;
+  if (!(eps >= 0.f) || isinf(eps)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t rows = (int64_t)B * L;
+  if (rows / 4 + 1 > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
+  const Range rx = span_bf16(x, rows, C, C);
+  const Range ry = y ? span_bf16(y, rows, C, C) : Range{0, 0};
+  const Range rxo = x_out ? span_bf16(x_out, rows, C, C) : Range{0, 0};
+  const Range rho = h_out ? span_bf16(h_out, rows, C, C) : Range{0, 0};
+  if (x_out && h_out && overlap(rxo, rho)) return WAN_ERROR_INVALID_VALUE;
+  if (bad_alias(x_out, rxo, C, x, rx, C) || bad_alias(x_out, rxo, C, y, ry, C) ||
+      bad_alias(h_out, rho, C, x, rx, C) || bad_alias(h_out, rho, C, y, ry, C))
+    return WAN_ERROR_INVALID_VALUE;
+
+  wan::AdaLNArgs a;
+  a.x_out = x_out;
+  a.h_out = h_out;
+  a.x = x;
+  a.y = y;
+  a.gate = y ? gate : nullptr;
+  a.shift = shift;
+  a.scale = scale;
+  a.rows = rows;
+  a.L = L;
+  a.C = C;
+  a.mod_stride_b = mod_stride_b;
+  a.mod_stride_l = mod_stride_l;
+  a.eps = eps;
+  return from_hip(wan::launch_adaln(a, stream));
+}
+
+}  // extern "C"

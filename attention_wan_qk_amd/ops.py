@@ -1,0 +1,158 @@
+"""Torch-facing wrappers of the libwanattn C ABI.
+
+Each function only checks tensor metadata, allocates outputs with torch and
+passes raw device pointers, sizes, strides and the current HIP stream to the
+library. All arithmetic happens in the library's kernels.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import WAN_NORM, WAN_NORM_PER_HEAD, WAN_ROPE, check, lib
+
+HEAD_DIM = 128
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _token_major(t: torch.Tensor, name: str, C: int):
+    """bf16 tensor [B, L, C] or [B, L, H, D] whose rows may be a column slice
+    of a wider buffer. Returns (B, L, ld)."""
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name}: expected a bf16 CUDA tensor, got {t.dtype} on {t.device}")
+    if t.dim() == 4:
+        B, L, H, D = t.shape
+        if H * D != C or t.stride(3) != 1 or t.stride(2) != D:
+            raise ValueError(f"{name}: heads must be contiguous [B, L, H, D] with H*D = {C}")
+    elif t.dim() == 3:
+        B, L, c = t.shape
+        if c != C or t.stride(2) != 1:
+            raise ValueError(f"{name}: expected [B, L, {C}] with unit channel stride")
+    else:
+        raise ValueError(f"{name}: expected a 3-D or 4-D tensor")
+    ld = t.stride(1) if L > 1 else max(C, t.stride(1))
+    if B > 1 and t.stride(0) != L * ld:
+        raise ValueError(f"{name}: batch stride must be L * row stride")
+    return B, L, ld
+
+
+def _channels(t: torch.Tensor) -> int:
+    return t.shape[2] * (t.shape[3] if t.dim() == 4 else 1)
+
+
+def qk_norm_rope3d(q, k, heads: int, grid, gain_q=None, gain_k=None, *, eps: float = 1e-6,
+                   theta: float = 10000.0, norm: bool = True, rope: bool = True,
+                   per_head: bool = False, q_out=None, k_out=None, inplace: bool = False):
+    """RMSNorm (times gain) and 3D RoPE of q and/or k; returns (q_out, k_out)."""
+    ref = q if q is not None else k
+    C = _channels(ref)
+    B, L, ld_in = _token_major(ref, "q" if q is not None else "k", C)
+    if q is not None and k is not None:
+        Bk, Lk, ldk = _token_major(k, "k", C)
+        if (Bk, Lk, ldk) != (B, L, ld_in):
+            raise ValueError("q and k must have the same shape and row stride")
+    if inplace:
+        q_out, k_out = q, k
+    else:
+        if q is not None and q_out is None:
+            q_out = torch.empty(B, L, C, dtype=torch.bfloat16, device=ref.device)
+        if k is not None and k_out is None:
+            k_out = torch.empty(B, L, C, dtype=torch.bfloat16, device=ref.device)
+    ld_out = _token_major(q_out if q_out is not None else k_out, "out", C)[2]
+    for g in (gain_q, gain_k):
+        if g is not None and (g.dtype != torch.float32 or g.numel() != C or not g.is_contiguous()):
+            raise ValueError("gains must be contiguous fp32 [H*D]")
+    flags = (WAN_NORM if norm else 0) | (WAN_ROPE if rope else 0) | \
+        (WAN_NORM_PER_HEAD if per_head else 0)
+    f, h, w = grid if grid is not None else (0, 0, 0)
+    st = lib().wan_qk_norm_rope3d(_ptr(q_out), _ptr(k_out), _ptr(q), _ptr(k), _ptr(gain_q),
+                                  _ptr(gain_k), B, L, heads, C // heads, f, h, w, ld_in,
+                                  ld_out, eps, theta, flags, _stream(ref))
+    check("wan_qk_norm_rope3d", st)
+    return q_out, k_out
+
+
+def self_attn_fwd(q, k, v, heads: int, k_lens=None, scale: float = 0.0, out=None,
+                  return_lse: bool = False):
+    """Full non-causal self-attention; returns o (and lse [B, H, L] fp32)."""
+    C = _channels(q)
+    B, L, ld_q = _token_major(q, "q", C)
+    _, _, ld_k = _token_major(k, "k", C)
+    _, _, ld_v = _token_major(v, "v", C)
+    if out is None:
+        out = torch.empty(B, L, C, dtype=torch.bfloat16, device=q.device)
+    ld_o = _token_major(out, "out", C)[2]
+    lse = torch.empty(B, heads, L, dtype=torch.float32, device=q.device) if return_lse else None
+    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
+        raise TypeError("k_lens must be a CUDA int32 tensor")
+    st = lib().wan_self_attn_fwd(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(k_lens), B, L, heads, C // heads, ld_q, ld_k, ld_v,
+                                 ld_o, scale, _stream(q))
+    check("wan_self_attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def cross_attn_fwd(q, k, v, heads: int, context_lens=None, scale: float = 0.0, out=None):
+    """Cross-attention of q [B, Lq, C] to k, v [B, Lk, C]; returns o."""
+    C = _channels(q)
+    B, Lq, ld_q = _token_major(q, "q", C)
+    _, Lk, ld_k = _token_major(k, "k", C)
+    _, _, ld_v = _token_major(v, "v", C)
+    if ld_k != ld_v:
+        raise ValueError("k and v must share one row stride")
+    if out is None:
+        out = torch.empty(B, Lq, C, dtype=torch.bfloat16, device=q.device)
+    ld_o = _token_major(out, "out", C)[2]
+    if context_lens is not None and (context_lens.dtype != torch.int32 or not context_lens.is_cuda):
+        raise TypeError("context_lens must be a CUDA int32 tensor")
+    st = lib().wan_cross_attn_fwd(_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(context_lens), B,
+                                  Lq, Lk, heads, C // heads, ld_q, ld_k, ld_o, scale,
+                                  _stream(q))
+    check("wan_cross_attn_fwd", st)
+    return out
+
+
+def _mod_strides(vecs, B, L, C):
+    strides = None
+    for v in vecs:
+        if v is None:
+            continue
+        if v.dtype != torch.float32 or not v.is_cuda or v.stride(-1) != 1:
+            raise ValueError("modulation vectors must be fp32 CUDA tensors with unit channel stride")
+        if v.dim() == 2 and tuple(v.shape) == (B, C):
+            s = (v.stride(0) if B > 1 else C, 0)
+        elif v.dim() == 3 and tuple(v.shape) == (B, L, C):
+            s = (v.stride(0) if B > 1 else L * v.stride(1), v.stride(1) if L > 1 else C)
+        else:
+            raise ValueError("modulation vectors must be [B, C] or [B, L, C]")
+        if strides is not None and s != strides:
+            raise ValueError("gate, shift and scale must share one layout")
+        strides = s
+    return strides or (C, 0)
+
+
+def adaln_modulate_gate(x, y=None, gate=None, shift=None, scale=None, eps: float = 1e-6, *,
+                        want_x: bool = True, want_h: bool = True, x_out=None, h_out=None):
+    """r = x + gate*y; returns (bf16(r) or None, bf16(LN(r)*(1+scale)+shift) or None)."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 3:
+        raise ValueError("x must be a contiguous bf16 [B, L, C] tensor")
+    B, L, C = x.shape
+    if y is not None and (y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous()):
+        raise ValueError("y must match x")
+    if want_x and x_out is None:
+        x_out = torch.empty_like(x)
+    if want_h and h_out is None:
+        h_out = torch.empty_like(x)
+    sb, sl = _mod_strides((gate, shift, scale), B, L, C)
+    st = lib().wan_adaln_modulate_gate(_ptr(x_out), _ptr(h_out), _ptr(x), _ptr(y), _ptr(gate),
+                                       _ptr(shift), _ptr(scale), B, L, C, sb, sl, eps,
+                                       _stream(x))
+    check("wan_adaln_modulate_gate", st)
+    return x_out, h_out

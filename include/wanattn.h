@@ -1,0 +1,205 @@
+/*
+ * wanattn: the attention sublayer of a Wan2.1/2.2 DiT block (WanAttentionBlock)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The four compute calls follow the block as the "Wan2.2 code walkthrough"
+ * page (newtid.com repost) shows it:
+ *
+ *   y = self_attn(norm1(x) * (1 + e[1]) + e[0], seq_lens, grid_sizes, freqs)
+ *         -> q/k RMSNorm, rope_apply(q), rope_apply(k), flash_attention(...)
+ *   x = x + y * e[2]
+ *   x = x + cross_attn(norm3(x), context, context_lens)
+ *
+ * and the paper deep dive "论文专题讲解：Wan2.1：开源视频生成系统路线"
+ * (section "Video DiT 与 Flow Matching": full spatio-temporal self-attention,
+ * cross-attention to the 512-token umT5 text context).
+ *
+ * The q/k/v and output projections between the calls are the caller's.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every call returns a wanStatus_t. Arguments are checked on the host
+ *   before anything is enqueued; on an error nothing is launched.
+ * - Tensor pointers are caller-owned DEVICE memory. bf16 tensors are passed
+ *   as void* holding IEEE bfloat16 bit patterns and must be 16-byte aligned;
+ *   fp32 vectors must be 16-byte aligned too.
+ * - The library allocates nothing, frees nothing, keeps no pointer and no
+ *   state between calls, and never synchronises: work is enqueued on
+ *   `stream` (NULL = the default stream) and device faults surface at the
+ *   caller's next synchronisation. Calls are reentrant and thread-safe.
+ * - Token-major tensors [B, L, H, D] address element (b, l, h, d) at
+ *   ptr[(b * L + l) * ld + h * D + d]; `ld` (elements between consecutive
+ *   tokens) may exceed H*D so that slices of a fused buffer can be passed;
+ *   ld = 0 means H*D. ld must be a multiple of 8.
+ * - D (head size) must be 128; otherwise WAN_ERROR_NOT_SUPPORTED.
+ * - A call whose B or L (Lq) is 0 has nothing to do and returns
+ *   WAN_SUCCESS without reading any pointer.
+ */
+#ifndef WANATTN_H_
+#define WANATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wanStatus {
+  WAN_SUCCESS = 0,
+  WAN_ERROR_INVALID_VALUE = 1,  /* bad pointer, size, stride, alias or flag */
+  WAN_ERROR_NOT_SUPPORTED = 2,  /* valid request outside what is built (D != 128, C too large) */
+  WAN_ERROR_LAUNCH = 3          /* the HIP runtime refused the launch */
+} wanStatus_t;
+
+/* Flags of wan_qk_norm_rope3d. */
+#define WAN_NORM 1u          /* RMSNorm of each token row, times the gain */
+#define WAN_ROPE 2u          /* 3D RoPE over the (f, h, w) grid */
+#define WAN_NORM_PER_HEAD 4u /* RMSNorm over each head's D channels instead of the H*D row */
+
+/* Static string for a status code. */
+const char* wan_status_string(wanStatus_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int wan_version(void);
+
+/*
+ * wan_qk_norm_rope3d: q/k RMSNorm fused with 3D RoPE.
+ *
+ * Passage: WanAttentionBlock self-attention (q/k RMSNorm, then
+ * rope_apply(q, grid_sizes, freqs) and rope_apply(k, ...); V is not rotated)
+ * and the 3D RoPE snippet of the "Wan2.2 code walkthrough" page: the
+ * d/2 = 64 complex frequencies of a head are split [c - 2(c//3), c//3, c//3]
+ * = 22/21/21 between the t, h and w axes, broadcast over the flattened grid
+ * (token n = (t*h + y)*w + x, w fastest) and applied as a complex multiply
+ * on interleaved (re, im) pairs. "初识wan系列模型" (huan-yin.github.io), "3D RoPE
+ * 坐标体系的建立与预计算", gives each token its (t, y, x) coordinates.
+ *
+ * For each token row r of q (and of k):
+ *   WAN_NORM:  r <- r / sqrt(mean(r^2) + eps) * gain   (mean over H*D, or over
+ *              each head's D with WAN_NORM_PER_HEAD; gain NULL = 1)
+ *   WAN_ROPE:  pair j of every head rotates by pos_a * theta^(-2 j' / D_a),
+ *              a = axis of j, j' = index of j inside that axis, D_a = 2 * (pairs
+ *              of that axis), pos = (t, y, x) of the token
+ * computed in fp32 and stored as bf16 (round to nearest even).
+ *
+ * q_out, k_out   bf16 [B, L, H, D], row stride ld_out. May equal q / k
+ *                (in place; then ld_out must equal ld_in).
+ * q, k           bf16 [B, L, H, D], row stride ld_in. Either may be NULL
+ *                (then its output must be NULL too), not both.
+ * gain_q, gain_k fp32 [H*D] RMSNorm gains, or NULL for 1.
+ * grid_f/h/w     latent-patch grid; with WAN_ROPE, f*h*w must equal L and each
+ *                of f, h, w must be in [1, 1024].
+ * eps            RMSNorm epsilon (>= 0), e.g. 1e-6.
+ * rope_theta     RoPE base (> 1), e.g. 10000.
+ * flags          any OR of WAN_NORM, WAN_ROPE, WAN_NORM_PER_HEAD (PER_HEAD only
+ *                with WAN_NORM).
+ * Errors: WAN_ERROR_INVALID_VALUE for NULL/misaligned pointers, bad sizes or
+ * strides, partial overlap between an input and an output, bad flags or a
+ * grid that does not match L; WAN_ERROR_NOT_SUPPORTED for D != 128 or
+ * H*D > 8192.
+ */
+wanStatus_t wan_qk_norm_rope3d(void* q_out, void* k_out, const void* q,
+                               const void* k, const float* gain_q,
+                               const float* gain_k, int B, int L, int H, int D,
+                               int grid_f, int grid_h, int grid_w,
+                               int64_t ld_in, int64_t ld_out, float eps,
+                               float rope_theta, unsigned flags,
+                               hipStream_t stream);
+
+/*
+ * wan_self_attn_fwd: full non-causal softmax self-attention.
+ *
+ * Passage: WanSelfAttention.forward on the "Wan2.2 code walkthrough" page,
+ * flash_attention(q = rope(q), k = rope(k), v, k_lens = seq_lens,
+ * window_size = (-1, -1)): a global window and no causal mask, so every video
+ * token attends to every token of past, present and future frames.
+ *
+ * For every (b, h) and query row i:
+ *   o[b,i,h,:] = sum_{j < n_b} softmax_j(scale * q_i . k_j) v_j,
+ *   n_b = clamp(k_lens[b], 0, L) (k_lens NULL: n_b = L),
+ *   lse[b,h,i] = log(sum_{j < n_b} exp(scale * q_i . k_j))  (natural log).
+ * n_b = 0 gives o = 0 and lse = -inf. bf16 MFMA products, fp32 accumulation,
+ * fp32 running max and sum; o is stored as bf16.
+ *
+ * o        bf16 [B, L, H, D], row stride ld_o; must not overlap q, k or v.
+ * lse      fp32 [B, H, L] or NULL; must not overlap the other tensors.
+ * q, k, v  bf16 [B, L, H, D], row strides ld_q, ld_k, ld_v.
+ * k_lens   device int32 [B] or NULL. Read on the device, so not checked on
+ *          the host: values are clamped to [0, L].
+ * softmax_scale  > 0, or <= 0 for 1/sqrt(D).
+ * Errors: WAN_ERROR_INVALID_VALUE (NULL/misaligned pointers, bad sizes or
+ * strides, o overlapping an input), WAN_ERROR_NOT_SUPPORTED (D != 128).
+ */
+wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q,
+                              const void* k, const void* v,
+                              const int32_t* k_lens, int B, int L, int H,
+                              int D, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                              int64_t ld_o, float softmax_scale,
+                              hipStream_t stream);
+
+/*
+ * wan_cross_attn_fwd: cross-attention of video tokens to text tokens.
+ *
+ * Passage: cross_attn(norm3(x), context, context_lens) in the WanAttentionBlock
+ * snippet of the "Wan2.2 code walkthrough" page; the context is the 512-token
+ * umT5 text embedding projected to the model width ("论文专题讲解：Wan2.1",
+ * section "Video DiT 与 Flow Matching"). No RoPE.
+ *
+ * Same arithmetic as wan_self_attn_fwd with Lq query rows and Lk keys:
+ *   o[b,i,h,:] = sum_{j < n_b} softmax_j(scale * q_i . k_j) v_j,
+ *   n_b = clamp(context_lens[b], 0, Lk) (NULL: Lk); n_b = 0 gives o = 0.
+ *
+ * o      bf16 [B, Lq, H, D], row stride ld_o; must not overlap q, k or v.
+ * q      bf16 [B, Lq, H, D], row stride ld_q.
+ * k, v   bf16 [B, Lk, H, D], row stride ld_kv (shared by k and v).
+ * context_lens  device int32 [B] or NULL.
+ * Errors: as wan_self_attn_fwd; Lk must be >= 1.
+ */
+wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k,
+                               const void* v, const int32_t* context_lens,
+                               int B, int Lq, int Lk, int H, int D,
+                               int64_t ld_q, int64_t ld_kv, int64_t ld_o,
+                               float softmax_scale, hipStream_t stream);
+
+/*
+ * wan_adaln_modulate_gate: residual update + AdaLN-modulated LayerNorm.
+ *
+ * Passage: the WanAttentionBlock snippet of the "Wan2.2 code walkthrough" page:
+ * e = (modulation + e).chunk(6) gives shift, scale, gate, shift2, scale2,
+ * gate2; norm1(x).float() * (1 + e[1]) + e[0] feeds self-attention;
+ * x = x + y * e[2] is the gated residual; x = x + cross_attn(norm3(x), ...)
+ * is the ungated one. norm1/norm2 are LayerNorms computed in fp32.
+ *
+ * Per token row (C channels), in fp32:
+ *   r = x + gate * y    (y NULL: r = x; gate NULL: r = x + y)
+ *   x_out = bf16(r)                                  (if x_out != NULL)
+ *   h_out = bf16((r - mean(r)) / sqrt(var(r) + eps) * (1 + scale) + shift)
+ *                                                    (if h_out != NULL)
+ * with the population variance and shift/scale NULL meaning 0. h is taken
+ * from the unrounded r. norm3 with affine (gamma, beta) is this call with
+ * scale = gamma - 1 and shift = beta.
+ *
+ * x_out, h_out  bf16 [B, L, C] dense; at least one non-NULL; they must not
+ *               overlap each other. Either may be the same pointer as x or
+ *               y (in place); partial overlaps are rejected.
+ * x, y          bf16 [B, L, C] dense; y may be NULL.
+ * gate, shift, scale  fp32, element (b, l, c) at ptr[b*mod_stride_b +
+ *               l*mod_stride_l + c]: mod_stride_l = 0 broadcasts one vector
+ *               per sample over the tokens (per-sample modulation, [B, 6, C]
+ *               chunks use mod_stride_b = 6C); mod_stride_l = C or 6C gives
+ *               per-token modulation. mod_stride_b = 0 means C.
+ * C must be a multiple of 8 and at most 8192.
+ */
+wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x,
+                                    const void* y, const float* gate,
+                                    const float* shift, const float* scale,
+                                    int B, int L, int C, int64_t mod_stride_b,
+                                    int64_t mod_stride_l, float eps,
+                                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WANATTN_H_ */

@@ -222,23 +222,28 @@ def rope3d_rotate(x, phi) -> np.ndarray:
 
 def qk_norm_rope3d(x, gain, grid, H: int, eps: float = 1e-6,
                    theta: float = 10000.0, norm: bool = True,
-                   rope: bool = True, per_head: bool = False) -> np.ndarray:
+                   rope: bool = True, per_head: bool = False,
+                   rows=None) -> np.ndarray:
     """RMSNorm (times gain) then 3D RoPE of one projected tensor.
 
-    x: [B, L, H*d] token-major rows; grid = (f, h, w) with f*h*w = L.
+    x: [B, L, H*d] token-major rows; grid = (f, h, w) with f*h*w = L. With
+    ``rows`` given, x holds only those token rows ([B, len(rows), H*d]) and
+    rows are their token indices in the grid.
     Self-attention snippet: ``rope_apply(q)`` / ``rope_apply(k)`` after the
     optional q/k RMSNorm; V is never rotated. With norm False the gain is not
     applied (it belongs to the norm).
     """
     x = _f64(x)
-    B, L, C = x.shape
+    B, R, C = x.shape
     d = C // H
     y = rms_norm(x, gain, eps, d if per_head else C) if norm else x.copy()
     if rope:
         f, hh, ww = grid
-        assert f * hh * ww == L
         phi = rope3d_angles(f, hh, ww, d, theta)
-        y = rope3d_rotate(y.reshape(B, L, H, d), phi).reshape(B, L, C)
+        assert rows is not None or phi.shape[0] == R
+        if rows is not None:
+            phi = phi[np.asarray(rows, dtype=np.int64)]
+        y = rope3d_rotate(y.reshape(B, R, H, d), phi).reshape(B, R, C)
     return y
 
 

@@ -1,0 +1,52 @@
+"""Comparison rule for bf16 outputs of the HIP path against the float64 oracle.
+
+Tolerance (bf16 inputs, fp32 accumulation): max-abs 1e-2 and mean-abs 1e-3,
+measured against the oracle's float64 result rounded to bf16 (nearest even),
+because the output itself is bf16. Where one bf16 quantum of the value
+exceeds 1e-2 (|v| >= 2), a single rounding-boundary flip between the
+kernel's fp32 value and the exact value costs one quantum, so the element
+bound there is that quantum; such flips must stay rare (<= 1e-3 of the
+elements), which rules out a systematic one-quantum error.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+MAX_FLIP_FRACTION = 1e-3
+
+
+def bf16_quantum(r: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |r| (2**(e-8) for |r| in [2**(e-1), 2**e))."""
+    _, e = np.frexp(np.abs(r))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def compare(name: str, got_bits: np.ndarray, ref64: np.ndarray, max_abs: float = MAX_ABS,
+            mean_abs: float = MEAN_ABS) -> dict:
+    got = O.bf16_bits_to_f64(got_bits)
+    ref = O.bf16_round(ref64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    d = np.abs(got - ref)
+    allowed = np.maximum(max_abs, bf16_quantum(ref))
+    over = d > max_abs
+    stats = {
+        "n": int(d.size),
+        "max_abs": float(d.max()) if d.size else 0.0,
+        "mean_abs": float(d.mean()) if d.size else 0.0,
+        "flips_over_1e-2": int(over.sum()),
+        "rel_l2": float(np.linalg.norm(got - ref64) / max(np.linalg.norm(ref64), 1e-300)),
+    }
+    print(f"[parity] {name}: {stats}", flush=True)
+    bad = d > allowed
+    assert not bad.any(), (
+        f"{name}: {int(bad.sum())} elements beyond tolerance; worst at "
+        f"{np.unravel_index(np.argmax(d - allowed), d.shape)}: {stats}")
+    assert stats["mean_abs"] <= mean_abs, f"{name}: mean-abs {stats['mean_abs']}"
+    assert over.sum() <= max(1, MAX_FLIP_FRACTION * d.size), f"{name}: too many flips {stats}"
+    return stats

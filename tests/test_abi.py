@@ -1,0 +1,159 @@
+"""The C ABI library: it loads, exports every call declared in
+include/wanattn.h, and rejects bad arguments on the host before launching
+anything. No kernel runs here (CPU only): every call below either fails a
+host check or has no work (B * L == 0)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wanattn.h")
+
+INV, NS, OK = 1, 2, 0
+A = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
+MB = 1 << 26
+
+
+@pytest.fixture(scope="module")
+def L():
+    from attention_wan_qk_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_wan_qk_amd.build import build
+        build(verbose=False)
+    return _lib.lib()
+
+
+def declared_calls():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(wan_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    calls = declared_calls()
+    for name in ("wan_qk_norm_rope3d", "wan_self_attn_fwd", "wan_cross_attn_fwd",
+                 "wan_adaln_modulate_gate", "wan_status_string", "wan_version"):
+        assert name in calls
+
+
+def test_library_exports_every_declared_symbol(L):
+    from attention_wan_qk_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (wan_\w+)", out))
+    for name in declared_calls():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert set(_lib.SIGNATURES) == set(declared_calls())
+
+
+def test_status_strings_and_version(L):
+    assert L.wan_status_string(0) == b"WAN_SUCCESS"
+    assert L.wan_status_string(1) == b"WAN_ERROR_INVALID_VALUE"
+    assert L.wan_status_string(2) == b"WAN_ERROR_NOT_SUPPORTED"
+    assert L.wan_status_string(3) == b"WAN_ERROR_LAUNCH"
+    assert L.wan_version() >= 100
+
+
+def norm_rope(L, **kw):
+    a = dict(q_out=A, k_out=A + MB, q=A + 2 * MB, k=A + 3 * MB, gq=None, gk=None, B=1, Lt=12,
+             H=2, D=128, f=1, h=3, w=4, ld_in=0, ld_out=0, eps=1e-6, theta=1e4, flags=3)
+    a.update(kw)
+    return L.wan_qk_norm_rope3d(a["q_out"], a["k_out"], a["q"], a["k"], a["gq"], a["gk"],
+                                a["B"], a["Lt"], a["H"], a["D"], a["f"], a["h"], a["w"],
+                                a["ld_in"], a["ld_out"], a["eps"], a["theta"], a["flags"], None)
+
+
+def test_norm_rope_rejections(L):
+    assert norm_rope(L, D=64) == NS
+    assert norm_rope(L, H=65) == NS                       # C > 8192
+    assert norm_rope(L, q=None, k=None, q_out=None, k_out=None) == INV
+    assert norm_rope(L, q=None) == INV                    # output without input
+    assert norm_rope(L, q=A + 2 * MB + 2) == INV          # misaligned
+    assert norm_rope(L, f=2) == INV                       # grid != L
+    assert norm_rope(L, h=1025, w=1, f=1, Lt=1025) == INV  # > table length
+    assert norm_rope(L, flags=8) == INV
+    assert norm_rope(L, flags=4) == INV                   # per-head without norm
+    assert norm_rope(L, ld_in=200) == INV                 # < C
+    assert norm_rope(L, ld_in=260) == INV                 # not a multiple of 8
+    assert norm_rope(L, eps=-1.0) == INV
+    assert norm_rope(L, theta=1.0) == INV
+    assert norm_rope(L, q_out=A + 2 * MB + 16) == INV     # partial overlap with q
+    assert norm_rope(L, q_out=A + 2 * MB, ld_out=512) == INV  # in place, stride differs
+    assert norm_rope(L, q_out=A + 3 * MB) == INV          # q_out == k (other input)
+    assert norm_rope(L, B=0) == OK                        # nothing to do
+    assert norm_rope(L, Lt=0) == OK
+
+
+def attn(L, **kw):
+    a = dict(o=A, lse=None, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, kl=None, B=1, Lt=64, H=2,
+             D=128, lq=0, lk=0, lv=0, lo=0, scale=0.0)
+    a.update(kw)
+    return L.wan_self_attn_fwd(a["o"], a["lse"], a["q"], a["k"], a["v"], a["kl"], a["B"],
+                               a["Lt"], a["H"], a["D"], a["lq"], a["lk"], a["lv"], a["lo"],
+                               a["scale"], None)
+
+
+def test_self_attn_rejections(L):
+    assert attn(L, D=64) == NS
+    assert attn(L, o=None) == INV
+    assert attn(L, v=None) == INV
+    assert attn(L, q=A + MB + 8) == INV
+    assert attn(L, o=A + MB) == INV                       # o aliases q
+    assert attn(L, o=A + 2 * MB + 256) == INV             # o overlaps k
+    assert attn(L, lse=A + 3 * MB) == INV                 # lse overlaps v
+    assert attn(L, lq=100) == INV
+    assert attn(L, lk=248) == INV                         # multiple of 8 but < C=256
+    assert attn(L, lo=260) == INV
+    assert attn(L, H=0) == INV
+    assert attn(L, B=-1) == INV
+    assert attn(L, scale=float("nan")) == INV
+    assert attn(L, scale=float("inf")) == INV
+    assert attn(L, B=0) == OK
+    assert attn(L, Lt=0) == OK
+
+
+def test_cross_attn_rejections(L):
+    def cross(**kw):
+        a = dict(o=A, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, cl=None, B=1, Lq=64, Lk=32, H=2,
+                 D=128, lq=0, lkv=0, lo=0, scale=0.0)
+        a.update(kw)
+        return L.wan_cross_attn_fwd(a["o"], a["q"], a["k"], a["v"], a["cl"], a["B"], a["Lq"],
+                                    a["Lk"], a["H"], a["D"], a["lq"], a["lkv"], a["lo"],
+                                    a["scale"], None)
+    assert cross(Lk=0) == INV
+    assert cross(D=96) == NS
+    assert cross(o=A + 3 * MB) == INV
+    assert cross(k=A + 2 * MB + 4) == INV
+    assert cross(Lq=0) == OK
+
+
+def test_adaln_rejections(L):
+    def adaln(**kw):
+        a = dict(xo=A, ho=A + MB, x=A + 2 * MB, y=A + 3 * MB, g=A + 4 * MB, sh=A + 5 * MB,
+                 sc=A + 6 * MB, B=1, Lt=8, C=256, sb=0, sl=0, eps=1e-6)
+        a.update(kw)
+        return L.wan_adaln_modulate_gate(a["xo"], a["ho"], a["x"], a["y"], a["g"], a["sh"],
+                                         a["sc"], a["B"], a["Lt"], a["C"], a["sb"], a["sl"],
+                                         a["eps"], None)
+    assert adaln(C=100) == INV                  # not a multiple of 8
+    assert adaln(C=8200) == NS
+    assert adaln(xo=None, ho=None) == INV
+    assert adaln(x=None) == INV
+    assert adaln(ho=A) == INV                   # x_out and h_out overlap
+    assert adaln(xo=A + 2 * MB + 16) == INV     # partial overlap with x
+    assert adaln(g=A + 4 * MB + 4) == INV       # misaligned modulation
+    assert adaln(sb=-8) == INV
+    assert adaln(eps=float("nan")) == INV
+    assert adaln(B=0) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from attention_wan_qk_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

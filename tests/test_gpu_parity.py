@@ -1,0 +1,228 @@
+"""Parity of the four library calls with the float64 oracle on the five
+Wan-shaped workloads (all rows for the tiny one, seeded sampled rows plus
+edge rows for the large ones), through the C ABI."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from attention_wan_qk_amd import ops, synth
+from attention_wan_qk_amd.workloads import WORKLOADS
+from tests._parity import compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+IDS = [w.name for w in WORKLOADS]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _rows(w):
+    return np.arange(w.tokens) if w.tokens <= 4096 else synth.sample_rows(w)
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", WORKLOADS, ids=IDS)
+def test_qk_norm_rope3d(w):
+    _announce(f"qk_norm_rope3d {w.name}")
+    q = synth.tensor(w, "q", DEV)
+    k = synth.tensor(w, "k", DEV)
+    gq = synth.tensor(w, "gain_q", DEV)
+    gk = synth.tensor(w, "gain_k", DEV)
+    qo, ko = ops.qk_norm_rope3d(q, k, w.heads, w.grid, gq, gk, eps=w.eps, theta=w.rope_theta)
+    torch.cuda.synchronize()
+    rows = _rows(w)
+    for name, x, g, out in (("q", q, gq, qo), ("k", k, gk, ko)):
+        ref = O.qk_norm_rope3d(synth.bf16_bits(x[:, rows]), g.cpu().numpy(), w.grid, w.heads,
+                               eps=w.eps, theta=w.rope_theta, rows=rows)
+        compare(f"{w.name} {name}", synth.bf16_bits(out[:, rows]), ref)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w", WORKLOADS, ids=IDS)
+def test_self_attn(w):
+    _announce(f"self_attn {w.name}")
+    q = synth.tensor(w, "q", DEV)
+    k = synth.tensor(w, "k", DEV)
+    v = synth.tensor(w, "v", DEV)
+    o, lse = ops.self_attn_fwd(q, k, v, w.heads, return_lse=True)
+    torch.cuda.synchronize()
+    rows = _rows(w)
+    ref_o, ref_lse = O.self_attention(synth.bf16_bits(q[:, rows]), synth.bf16_bits(k),
+                                      synth.bf16_bits(v), w.heads)
+    compare(f"{w.name} o", synth.bf16_bits(o[:, rows]), ref_o)
+    got_lse = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_lse - ref_lse)) < 1e-3
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", WORKLOADS, ids=IDS)
+def test_cross_attn(w):
+    _announce(f"cross_attn {w.name}")
+    q = synth.tensor(w, "cross_q", DEV)
+    k = synth.tensor(w, "text_k", DEV)
+    v = synth.tensor(w, "text_v", DEV)
+    o = ops.cross_attn_fwd(q, k, v, w.heads)
+    torch.cuda.synchronize()
+    rows = _rows(w)
+    ref, _ = O.cross_attention(synth.bf16_bits(q[:, rows]), synth.bf16_bits(k),
+                               synth.bf16_bits(v), w.heads)
+    compare(f"{w.name} cross o", synth.bf16_bits(o[:, rows]), ref)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", WORKLOADS, ids=IDS)
+def test_adaln_modulate_gate(w):
+    _announce(f"adaln {w.name}")
+    x = synth.tensor(w, "x", DEV)
+    y = synth.tensor(w, "y", DEV)
+    e = synth.tensor(w, "mod", DEV)   # [B, 6, C]: shift, scale, gate, shift2, scale2, gate2
+    rows = _rows(w)
+    xb, yb = synth.bf16_bits(x[:, rows]), synth.bf16_bits(y[:, rows])
+    eh = e.cpu().numpy().astype(np.float64)
+    # norm1 + modulate (no residual)
+    _, h1 = ops.adaln_modulate_gate(x, None, None, e[:, 0], e[:, 1], w.eps, want_x=False)
+    # gated residual + norm3 (gamma = 1, beta = 0 -> scale = shift = 0)
+    x2, h3 = ops.adaln_modulate_gate(x, y, e[:, 2], None, None, w.eps)
+    # ungated residual only
+    x3, _ = ops.adaln_modulate_gate(x, y, None, None, None, w.eps, want_h=False)
+    torch.cuda.synchronize()
+    _, r1 = O.adaln_modulate_gate(xb, None, None, eh[:, 0], eh[:, 1], w.eps)
+    compare(f"{w.name} norm1-modulate", synth.bf16_bits(h1[:, rows]), r1)
+    r2, r3 = O.adaln_modulate_gate(xb, yb, eh[:, 2], None, None, w.eps)
+    compare(f"{w.name} gate-residual", synth.bf16_bits(x2[:, rows]), r2)
+    compare(f"{w.name} norm3", synth.bf16_bits(h3[:, rows]), r3)
+    r4, _ = O.adaln_modulate_gate(xb, yb, None, None, None, w.eps)
+    compare(f"{w.name} residual", synth.bf16_bits(x3[:, rows]), r4)
+
+
+# ----------------------------------------------------------------- edges ----
+def _rand(shape, seed, std=1.0):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (1, 7, 1), (2, 63, 3), (1, 64, 2), (2, 65, 1),
+                                   (1, 129, 2), (1, 200, 1), (2, 383, 2)])
+def test_self_attn_ragged(B, L, H):
+    _announce(f"self_attn ragged B={B} L={L} H={H}")
+    C = 128 * H
+    q, k, v = (_rand((B, L, C), s) for s in (1, 2, 3))
+    kl = torch.tensor([L, max(1, L // 2 + 1)][:B], dtype=torch.int32)
+    o, lse = ops.self_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, k_lens=kl.to(DEV),
+                               return_lse=True)
+    torch.cuda.synchronize()
+    qb, kb, vb = (synth.bf16_bits(t) for t in (q, k, v))
+    ref, rl = O.self_attention(qb, kb, vb, H, kl.numpy())
+    compare(f"ragged {B}x{L}x{H}", synth.bf16_bits(o), ref)
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3
+
+
+@pytest.mark.parametrize("Lk", [1, 7, 32, 511, 512, 513])
+def test_cross_attn_key_lengths(Lk):
+    _announce(f"cross_attn Lk={Lk}")
+    B, Lq, H = 2, 150, 2
+    C = 128 * H
+    q = _rand((B, Lq, C), 4)
+    k = _rand((B, Lk, C), 5)
+    v = _rand((B, Lk, C), 6)
+    cl = torch.tensor([Lk, max(1, Lk // 2 + 1)], dtype=torch.int32)
+    o = ops.cross_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, context_lens=cl.to(DEV))
+    torch.cuda.synchronize()
+    ref, _ = O.cross_attention(synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v), H,
+                               cl.numpy())
+    compare(f"cross Lk={Lk}", synth.bf16_bits(o), ref)
+
+
+def test_attn_empty_keys_and_peaked_logits():
+    _announce("self_attn k_len=0 and peaked")
+    B, L, H = 2, 96, 2
+    C = 128 * H
+    q, k, v = (_rand((B, L, C), s) for s in (7, 8, 9))
+    kl = torch.tensor([0, 40], dtype=torch.int32)
+    o, lse = ops.self_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, k_lens=kl.to(DEV),
+                               return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ref, _ = O.self_attention(*(synth.bf16_bits(t) for t in (q, k, v)), H, kl.numpy())
+    compare("k_len 0/40", synth.bf16_bits(o), ref)
+    # peaked: scale 4/sqrt(d) gives logits of std ~4 (position/scale bugs change o by O(1))
+    sc = 4.0 / math.sqrt(128)
+    o2 = ops.self_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, scale=sc)
+    torch.cuda.synchronize()
+    ref2, _ = O.self_attention(*(synth.bf16_bits(t) for t in (q, k, v)), H, scale=sc)
+    compare("peaked", synth.bf16_bits(o2), ref2)
+
+
+@pytest.mark.parametrize("flags", ["norm+rope", "norm", "rope", "per_head_norm+rope"])
+def test_norm_rope_flags_and_fused_buffer(flags):
+    _announce(f"norm_rope flags={flags}")
+    B, grid, H = 2, (3, 5, 7), 3
+    L, C = 105, 384
+    norm = "norm" in flags
+    rope = "rope" in flags
+    per_head = "per_head" in flags
+    qkv = _rand((B, L, 3 * C), 11, std=2.0).to(DEV)       # fused projection buffer
+    gq = (1 + 0.1 * torch.randn(C, generator=torch.Generator().manual_seed(3))).float()
+    gk = (1 + 0.1 * torch.randn(C, generator=torch.Generator().manual_seed(4))).float()
+    ref_in = synth.bf16_bits(qkv)
+    q, k = qkv[..., :C], qkv[..., C:2 * C]
+    ops.qk_norm_rope3d(q, k, H, grid, gq.to(DEV), gk.to(DEV), norm=norm, rope=rope,
+                       per_head=per_head, inplace=True)
+    torch.cuda.synchronize()
+    out = synth.bf16_bits(qkv)
+    for name, sl, g in (("q", slice(0, C), gq), ("k", slice(C, 2 * C), gk)):
+        ref = O.qk_norm_rope3d(ref_in[..., sl], g.numpy(), grid, H, norm=norm, rope=rope,
+                               per_head=per_head)
+        compare(f"fused {flags} {name}", out[..., sl], ref)
+    assert np.array_equal(out[..., 2 * C:], ref_in[..., 2 * C:])   # v untouched
+
+
+def test_adaln_per_token_modulation_and_inplace():
+    _announce("adaln per-token + in place")
+    B, L, C = 2, 33, 1536
+    x = _rand((B, L, C), 21).to(DEV)
+    y = _rand((B, L, C), 22).to(DEV)
+    e = (torch.randn(B, L, 6, C, generator=torch.Generator().manual_seed(5)) * 0.3).float()
+    ed = e.to(DEV)
+    xb, yb = synth.bf16_bits(x), synth.bf16_bits(y)
+    x_work = x.clone()
+    xo, ho = ops.adaln_modulate_gate(x_work, y, ed[:, :, 2], ed[:, :, 0], ed[:, :, 1], 1e-6,
+                                     x_out=x_work)
+    torch.cuda.synchronize()
+    en = e.numpy().astype(np.float64)
+    r, h = O.adaln_modulate_gate(xb, yb, en[:, :, 2], en[:, :, 0], en[:, :, 1], 1e-6)
+    compare("per-token x'", synth.bf16_bits(xo), r)
+    compare("per-token h", synth.bf16_bits(ho), h)
+
+
+def test_determinism_and_side_stream():
+    _announce("determinism + side stream")
+    w = WORKLOADS[0]
+    q, k, v = (synth.tensor(w, t, DEV) for t in ("q", "k", "v"))
+    o1 = ops.self_attn_fwd(q, k, v, w.heads)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2 = ops.self_attn_fwd(q, k, v, w.heads)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

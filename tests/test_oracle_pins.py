@@ -392,3 +392,14 @@ def test_oracle_is_independent_of_the_library():
                         assert not m.startswith("attention_wan_qk_amd"), name
                         assert m.split(".")[0] in ("numpy", "__future__", "") or \
                             m.startswith("wan_oracle"), (name, m)
+
+
+def test_qk_norm_rope3d_row_subset_equals_full():
+    B, grid, H = 2, (3, 4, 5), 2
+    L, C = 60, 256
+    x = RNG.standard_normal((B, L, C))
+    g = 1 + 0.1 * RNG.standard_normal(C)
+    full = O.qk_norm_rope3d(x, g, grid, H)
+    rows = np.array([0, 7, 33, 59])
+    sub = O.qk_norm_rope3d(x[:, rows], g, grid, H, rows=rows)
+    assert np.array_equal(sub, full[:, rows])
