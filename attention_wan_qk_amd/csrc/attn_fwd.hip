@@ -11,7 +11,7 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16. K (A operand, keys x dims) is
 //    read from LDS; Q (B operand) stays in registers for the whole loop. In
 //    the accumulator each lane owns one query row (lane % 32) and 16 keys, so
-//    the row max needs one exchange with the other half-wave and the row sum
+//    the row max needs one half-wave swap (v_permlane32_swap) and the row sum
 //    none until the end.
 //  * O^T += V^T P^T on the same MFMA. P comes straight from the score
 //    registers (converted to bf16); V^T is read from the row-major V tile with
@@ -19,9 +19,12 @@
 //  * The running max is in log2 units of the scaled scores; it is only moved
 //    (and O, l rescaled) when some row's tile max exceeds it by more than 8,
 //    so the exponentials stay <= 2^8 and the rescale is rare.
-//  * K/V tiles are double-buffered in LDS (XOR-swizzled 16-byte chunks for
-//    conflict-free MFMA operand reads); the next tile's global loads are
-//    issued before the current tile's math.
+//  * K/V tiles are double-buffered in LDS: the buffer loads of tile t+1 are
+//    issued before tile t's math and stored to LDS after it. Rows past k_len
+//    fall outside the buffer resource and read as zero. Each 16-byte chunk of
+//    a row is XOR-swizzled so the MFMA operand reads are bank-conflict free;
+//    the loads pick, for lane i, the global chunk that belongs at
+//    base + 16 i, so the stores stay lane-linear.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
 #include "wan_device.h"
@@ -31,40 +34,45 @@ namespace wan {
 
 namespace {
 
-constexpr int kBM = 128;        // query rows per workgroup
-constexpr int kBN = 64;         // keys per tile
-constexpr int kHD = 128;        // head size
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;             // query rows per workgroup
+constexpr int kBN = 64;                      // keys per tile
+constexpr int kHD = 128;                     // head size
 constexpr int kRowBytes = kHD * 2;
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB
-constexpr int kThreads = 256;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB per load instruction
 constexpr float kRescaleThreshold = 8.0f;    // log2 units
+constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
-  return *reinterpret_cast<const bf16x8*>(base + off);
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+__device__ __forceinline__ bf16x8 lds_read16(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
 }
 
-__device__ __forceinline__ s16x4 lds_read_tr(const char* base, uint32_t off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+__device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-// Byte offset of 16-byte chunk `ch` of key row `key` in the K tile. The
-// chunk index is XORed with key % 16 so that 16 consecutive keys reading the
-// same logical chunk hit 16 different bank groups.
-__device__ __forceinline__ uint32_t k_off(int key, int ch) {
-  return (uint32_t)(key * kRowBytes + ((ch ^ (key & 15)) << 4));
-}
-// V tile: the transposed reads touch 4 consecutive keys x 4 consecutive
-// chunks per half-wave, so the chunk is XORed with 4 * (key % 4).
-__device__ __forceinline__ uint32_t v_off(int key, int ch) {
-  return (uint32_t)(key * kRowBytes + ((ch ^ ((key & 3) << 2)) << 4));
-}
+// K tile: 16-byte chunk ch of key row r lives at chunk ch ^ (r % 16), so the
+// 16 keys read together at one logical chunk hit 16 different bank groups.
+__device__ __forceinline__ int k_phys(int r, int ch) { return ch ^ (r & 15); }
+// V tile: a transposed read touches 4 consecutive keys x 4 consecutive
+// chunks per half-wave, so the chunk is XORed with 4 * (r % 4).
+__device__ __forceinline__ int v_phys(int r, int ch) { return ch ^ ((r & 3) << 2); }
 
 }  // namespace
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+  char* const Ks = smem;                    // K tiles, buffers 0 and 1
+  char* const Vs = smem + 2 * kTileBytes;   // V tiles, buffers 0 and 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,22 +90,74 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
 
   int kv_len = a.Lk;
   if (a.k_lens) kv_len = min(max(a.k_lens[b], 0), a.Lk);
+  const int nT = (kv_len + kBN - 1) / kBN;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.Lq * a.ld_q + h * kHD;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)b * a.Lk * a.ld_k + h * kHD;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (int64_t)b * a.Lk * a.ld_v + h * kHD;
+  const uint32_t row_k = (uint32_t)a.ld_k * 2, row_v = (uint32_t)a.ld_v * 2;
+  // Bytes of valid keys behind each base: anything past them reads as 0.
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)(kv_len * row_k), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
+
+  // Per-lane global offsets of this wave's tile loads: load i of wave w
+  // fills tile rows 4(4w + i) .. +3; lane l stores physical chunk l % 16 of
+  // row 4(4w + i) + l / 16, which holds logical chunk (l % 16) ^ swizzle.
+  uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int r = (wave * kLoadsPerWave + i) * 4 + (lane >> 4);
+    const int p = lane & 15;
+    vo_k[i] = r * row_k + (k_phys(r, p) << 4);  // k_phys is an involution
+    vo_v[i] = r * row_v + (v_phys(r, p) << 4);
+  }
+  u32x4 kreg[kLoadsPerWave], vreg[kLoadsPerWave];
+  auto issue = [&](int t) {
+    const uint32_t sk = (uint32_t)t * kBN * row_k, sv = (uint32_t)t * kBN * row_v;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k[i], sk, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_v[i], sv, 0);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int off = buf * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16;
+      *reinterpret_cast<u32x4*>(Ks + off) = kreg[i];
+      *reinterpret_cast<u32x4*>(Vs + off) = vreg[i];
+    }
+  };
 
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
   const int qrow = qt * kBM + wave * 32 + r32;
   bf16x8 qf[8];
-  if (qrow < a.Lq) {
-    const uint16_t* qr = qg + (int64_t)qrow * a.ld_q + 8 * hf;
+  {
+    const uint16_t* qr = qg + (int64_t)min(qrow, a.Lq - 1) * a.ld_q + 8 * hf;
 #pragma unroll
     for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
+
+  if (nT > 0) {
+    issue(0);
+    stage(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // Q and tile 0 have landed
+  __syncthreads();
+
+  // LDS read addresses (byte offsets inside a tile; the buffer, the 32-key
+  // block and the key chunk are immediate offsets).
+  int ka[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) ka[c] = r32 * kRowBytes + (k_phys(r32, 2 * c + hf) << 4);
+  const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
+  int va[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    va[db] = (4 * (g16 >> 1) + e4) * kRowBytes +
+             ((4 * (db ^ e4) + 2 * (g16 & 1) + (q4 >> 1)) << 4) + 8 * (q4 & 1);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -105,60 +165,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m_used = -INFINITY;
-  float lsum = 0.f;
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
 
-  const int nT = (kv_len + kBN - 1) / kBN;
-
-  // Tile staging: thread tid moves 16-byte chunks tid + 256 i (i < 4) of the
-  // 64 x 16 chunk tile; rows past kv_len are zero-filled (P is exactly 0
-  // there, and 0 * 0 keeps O finite).
-  u32x4 kreg[4], vreg[4];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = t * kBN + (idx >> 4);
-      const int ch = idx & 15;
-      if (key < kv_len) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * a.ld_k + 8 * ch);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * a.ld_v + 8 * ch);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = idx >> 4;
-      const int ch = idx & 15;
-      *reinterpret_cast<u32x4*>(&smem[buf][0][k_off(key, ch)]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][v_off(key, ch)]) = vreg[i];
-    }
-  };
-
-  if (nT > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  // Per-lane constants of the transposed V read (this lane as a source lane
-  // of ds_read_b64_tr_b16: group g = lane / 16, key step e4, dim quad q4).
-  const int g16 = lane >> 4;
-  const int e4 = (lane & 15) >> 2;
-  const int q4 = lane & 3;
-  const int vkey_base = 4 * (g16 >> 1) + e4;
-  const int vbyte_base = 32 * (g16 & 1) + 8 * q4;
-
-  for (int t = 0; t < nT; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nT) gload(t + 1);
+  auto body = [&](auto bufc, int t) {
+    constexpr int buf = decltype(bufc)::value;
+    if (t + 1 < nT) issue(t + 1);
 
     // ---- S^T = K Q^T for 64 keys: two 32-key blocks x 8 dim steps.
-    const char* Kt = smem[buf][0];
+    const char* Kt = Ks + buf * kTileBytes;
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -168,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = lds_read16(Kt, k_off(kb * 32 + r32, 2 * c + hf));
+        const bf16x8 kf = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
       }
     }
@@ -185,62 +199,81 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     }
 
     // ---- online softmax (log2 domain)
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mt = mx * a.scale_log2;
     if (__any(mt > m_used + kRescaleThreshold)) {
       const float mn = fmaxf(m_used, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
-      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ls[i] *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
       m_used = mn;
     }
+    const float neg_m = -m_used;
     bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, -m_used));
-        lsum += p[e];
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
+        ls[e & 3] += p[e];
       }
       f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
       pf[kc] = __builtin_convertvector(pv, bf16x8);
     }
 
     // ---- O^T += V^T P^T: 4 dim blocks x 4 key chunks of 16.
-    const char* Vt = smem[buf][1];
+    const char* Vt = Vs + buf * kTileBytes;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
+      const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int key0 = 32 * (kc >> 1) + 16 * (kc & 1) + vkey_base;
-        const int byte = 64 * db + vbyte_base;
-        const uint32_t o0 = v_off(key0, byte >> 4) + (byte & 15);
-        const uint32_t o1 = v_off(key0 + 8, byte >> 4) + (byte & 15);
-        const s16x4 lo = lds_read_tr(Vt, o0);
-        const s16x4 hi = lds_read_tr(Vt, o1);
+        const s16x4 lo = lds_read_tr(Vt + va[db] + krow * kRowBytes);
+        const s16x4 hi = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
         const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, cat), pf[kc], oacc[db], 0, 0, 0);
       }
     }
 
-    if (t + 1 < nT) swrite(buf ^ 1);
-    __syncthreads();
+    if (t + 1 < nT) {
+      // Buffer buf ^ 1 was last read in iteration t - 1, which every wave
+      // finished before the barrier that ended it.
+      stage(buf ^ 1);
+      __syncthreads();
+    }
+  };
+
+  int t = 0;
+  for (; t + 1 < nT; t += 2) {
+    body(Int<0>{}, t);
+    body(Int<1>{}, t + 1);
   }
+  if (t < nT) body(Int<0>{}, t);
 
   // ---- epilogue: combine the two half-waves' partial sums, normalise, store.
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                     false, false);
+    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (qrow < a.Lq) {
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -254,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     if (a.lse && hf == 0) {
       a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
-          ltot > 0.f ? m_used * 0.6931471805599453f + logf(ltot) : -INFINITY;
+          lsum > 0.f ? m_used * 0.6931471805599453f + logf(lsum) : -INFINITY;
     }
   }
 }

@@ -83,6 +83,9 @@ wanStatus_t check_attn(void* o, const float* lse, const void* q, const void* k,
       return WAN_ERROR_INVALID_VALUE;
   }
   if ((int64_t)B * H * ((Lq + 127) / 128) > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
+  // K/V of one (batch, head) are addressed with 32-bit byte offsets.
+  if ((int64_t)Lk * (ld_k > ld_v ? ld_k : ld_v) * 2 > (int64_t)0xffffffff)
+    return WAN_ERROR_NOT_SUPPORTED;
   return WAN_SUCCESS;
 }
 

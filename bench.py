@@ -1,0 +1,244 @@
+"""Benchmark of the Wan attention sublayer (one block's library calls).
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+  adaln (norm1 + modulate) -> qk RMSNorm + 3D RoPE -> self-attention ->
+  gated residual + norm3 -> cross q/k RMSNorm -> cross-attention ->
+  cross residual.
+The projection GEMMs between the calls are not part of the library; their
+outputs are synthetic tensors of the same shape.
+
+Prints one JSON line (rank 0). `value` is the self-attention FLOP of a step
+(4 L^2 d H B) divided by the whole step's time; the roofline object reports
+the self-attention kernel alone, timed with events on its stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="a14b-720p-cfg")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the oracle sample on the host")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="first run one device copy of this many MiB (a kernel of known "
+                        "traffic, to scale HBM byte counters)")
+    return p.parse_args()
+
+
+def kernel_source_sha(name: str) -> str:
+    path = os.path.join(ROOT, "attention_wan_qk_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is absent or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel, {}).get(workload)
+    if not rec or rec.get("source_sha") != kernel_source_sha(rec["source"]):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(w, tensors, budget_s: float):
+    """The float64 oracle on the host, on a bounded sample of the same
+    self-attention problem: 256 query rows of as many (batch, head) pairs as
+    fit the time budget. Reported in the metric's unit (TFLOP/s)."""
+    import numpy as np
+
+    import oracle as O
+    from attention_wan_qk_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = tensors
+    d = w.head_dim
+    rows = synth.sample_rows(w)[:256]
+    flop = 0.0
+    pairs = 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        for h in range(w.heads):
+            sl = slice(h * d, (h + 1) * d)
+            qb = synth.bf16_bits(q[b, rows, sl])
+            kb = synth.bf16_bits(k[b, :, sl])
+            vb = synth.bf16_bits(v[b, :, sl])
+            O.attention(qb, kb, vb, w.tokens, 1.0 / np.sqrt(d))
+            flop += 4.0 * len(rows) * w.tokens * d
+            pairs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"self-attention of {len(rows)} query rows x {pairs} (batch, head) pairs of "
+                  f"{w.name} (L={w.tokens}), float64 NumPy, {dt:.1f} s incl. host copies",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_wan_qk_amd import _lib, ops, synth
+    from attention_wan_qk_amd.workloads import BY_NAME
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_wan_qk_amd.build import build
+        build()
+    w = BY_NAME[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    B, L, C, H, Lt = w.batch, w.tokens, w.dim, w.heads, w.text_len
+
+    t = {n: synth.tensor(w, n, dev) for n in
+         ("x", "y", "q", "k", "v", "text_k", "text_v", "cross_q", "cross_y",
+          "gain_q", "gain_k", "gain_cq", "gain_ck", "mod")}
+    e = t["mod"]
+    emp = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+    h1, qr, kr, o = emp(B, L, C), emp(B, L, C), emp(B, L, C), emp(B, L, C)
+    x2, h3, cq, ck = emp(B, L, C), emp(B, L, C), emp(B, L, C), emp(B, Lt, C)
+    oc, x3 = emp(B, L, C), emp(B, L, C)
+    torch.cuda.synchronize()
+
+    names = ["adaln_norm1", "qk_norm_rope3d", "self_attn", "gate_norm3", "cross_qk_norm",
+             "cross_attn", "cross_residual"]
+    # algorithmic HBM bytes per call (bf16 = 2 B): reads + writes of token rows
+    E = B * L * C
+    bytes_per = {"adaln_norm1": 4 * E, "qk_norm_rope3d": 8 * E, "gate_norm3": 8 * E,
+                 "cross_qk_norm": 4 * E + 4 * B * Lt * C, "cross_residual": 6 * E}
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ops.adaln_modulate_gate(t["x"], None, None, e[:, 0], e[:, 1], w.eps, want_x=False,
+                                h_out=h1)
+        mark(1)
+        ops.qk_norm_rope3d(t["q"], t["k"], H, w.grid, t["gain_q"], t["gain_k"], eps=w.eps,
+                           theta=w.rope_theta, q_out=qr, k_out=kr)
+        mark(2)
+        ops.self_attn_fwd(qr, kr, t["v"], H, out=o)
+        mark(3)
+        ops.adaln_modulate_gate(t["x"], t["y"], e[:, 2], None, None, w.eps, x_out=x2, h_out=h3)
+        mark(4)
+        ops.qk_norm_rope3d(t["cross_q"], None, H, None, t["gain_cq"], None, eps=w.eps,
+                           rope=False, q_out=cq)
+        ops.qk_norm_rope3d(None, t["text_k"], H, None, None, t["gain_ck"], eps=w.eps,
+                           rope=False, k_out=ck)
+        mark(5)
+        ops.cross_attn_fwd(cq, ck, t["text_v"], H, out=oc)
+        mark(6)
+        ops.adaln_modulate_gate(x2, t["cross_y"], None, None, None, w.eps, want_h=False,
+                                x_out=x3)
+        mark(7)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per = {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+
+    attn_flop = w.self_attn_flop()
+    attn_tflops = attn_flop / (per["self_attn"] * 1e-3) / 1e12
+    breakdown = {}
+    for n in names:
+        rec = {"ms": round(per[n], 4)}
+        if n == "self_attn":
+            rec.update(tflops=round(attn_tflops, 1), frac_mfma=round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4))
+        elif n == "cross_attn":
+            tf = w.cross_attn_flop() / (per[n] * 1e-3) / 1e12
+            rec.update(tflops=round(tf, 1), frac_mfma=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+        else:
+            gbs = bytes_per[n] / (per[n] * 1e-3) / 1e9
+            rec.update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        breakdown[n] = rec
+    print(json.dumps({"breakdown": breakdown}), file=sys.stderr, flush=True)
+
+    traffic = measured_traffic("attn_fwd_kernel", w.name)
+    result = {
+        "metric": "self-attn TFLOP/s (4*L^2*d*H*B) at A14B 720P CFG (75600 tok), whole block step",
+        "value": round(attn_flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.1) modulation, 1+0.1N gains)",
+        "config": {"workload": w.name, "batch": B, "tokens": L, "grid": list(w.grid),
+                   "heads": H, "head_dim": w.head_dim, "text_len": Lt,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel (self-attention)",
+            "achieved": round(attn_tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, (t["q"], t["k"], t["v"]), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
