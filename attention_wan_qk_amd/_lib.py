@@ -5,7 +5,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwanattn.so")
+# WANATTN_LIB points the binding at another build of the same library.
+LIB_PATH = os.environ.get("WANATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libwanattn.so")
 
 WAN_SUCCESS = 0
 WAN_ERROR_INVALID_VALUE = 1

@@ -34,7 +34,13 @@ namespace wan {
 
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef WAN_ATTN_WAVES
+#define WAN_ATTN_WAVES 4
+#endif
+#ifndef WAN_ATTN_SETPRIO
+#define WAN_ATTN_SETPRIO 0
+#endif
+constexpr int kWaves = WAN_ATTN_WAVES;
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
 constexpr int kHD = 128;                     // head size
@@ -69,7 +75,7 @@ __device__ __forceinline__ int v_phys(int r, int ch) { return ch ^ ((r & 3) << 2
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
   char* const Ks = smem;                    // K tiles, buffers 0 and 1
   char* const Vs = smem + 2 * kTileBytes;   // V tiles, buffers 0 and 1
@@ -172,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     if (t + 1 < nT) issue(t + 1);
 
     // ---- S^T = K Q^T for 64 keys: two 32-key blocks x 8 dim steps.
+    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     const char* Kt = Ks + buf * kTileBytes;
     f32x16 s[2];
 #pragma unroll
@@ -187,6 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
+    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // ---- mask keys past kv_len (last tile only)
     if ((t + 1) * kBN > kv_len) {
 #pragma unroll
@@ -236,6 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     }
 
     // ---- O^T += V^T P^T: 4 dim blocks x 4 key chunks of 16.
+    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     const char* Vt = Vs + buf * kTileBytes;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -250,6 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
+    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (t + 1 < nT) {
       // Buffer buf ^ 1 was last read in iteration t - 1, which every wave
       // finished before the barrier that ended it.
