@@ -4,10 +4,11 @@
 // Follows the self-attention call of the "Wan2.2 code walkthrough" page,
 // flash_attention(q, k, v, k_lens, window_size = (-1, -1)): global window,
 // no causal mask, keys at or past k_lens[b] excluded. The L x L score matrix
-// is never stored: each workgroup owns 128 query rows of one (batch, head)
+// is never stored: each workgroup owns 256 query rows of one (batch, head)
 // and streams the keys in tiles of 64 with a running (online) softmax.
 //
-// Layout of the work (per workgroup: 4 wavefronts x 32 query rows):
+// Layout of the work (per workgroup: 8 wavefronts x 32 query rows, two per
+// SIMD):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16. K (A operand, keys x dims) is
 //    read from LDS; Q (B operand) stays in registers for the whole loop. In
 //    the accumulator each lane owns one query row (lane % 32) and 16 keys, so
@@ -16,15 +17,21 @@
 //  * O^T += V^T P^T on the same MFMA. P comes straight from the score
 //    registers (converted to bf16); V^T is read from the row-major V tile with
 //    ds_read_b64_tr_b16, whose key order is chosen to match P's.
+//  * Ping-pong: waves 0-3 and 4-7 run the same phase sequence one phase
+//    apart (GEMM phase: P V of tile j-1 then S of tile j; softmax phase of
+//    tile j), separated by workgroup barriers, so each SIMD always hosts one
+//    wave feeding the MFMA pipe while the other runs the softmax on the VALU.
+//  * Inside a GEMM phase the LDS operand reads are issued a few fragments
+//    ahead of their MFMAs (scheduling groups), hiding LDS latency.
 //  * The running max is in log2 units of the scaled scores; it is only moved
 //    (and O, l rescaled) when some row's tile max exceeds it by more than 8,
 //    so the exponentials stay <= 2^8 and the rescale is rare.
-//  * K/V tiles are double-buffered in LDS: the buffer loads of tile t+1 are
-//    issued before tile t's math and stored to LDS after it. Rows past k_len
-//    fall outside the buffer resource and read as zero. Each 16-byte chunk of
-//    a row is XOR-swizzled so the MFMA operand reads are bank-conflict free;
-//    the loads pick, for lane i, the global chunk that belongs at
-//    base + 16 i, so the stores stay lane-linear.
+//  * K/V tiles are double-buffered in LDS; the buffer loads of the next tiles
+//    are in flight during two phases before they are stored to LDS. Rows past
+//    k_len fall outside the buffer resource and read as zero. Each 16-byte
+//    chunk of a row is XOR-swizzled so the MFMA operand reads are
+//    bank-conflict free; the loads pick, for lane i, the global chunk that
+//    belongs at base + 16 i, so the stores stay lane-linear.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
 #include "wan_device.h"
@@ -34,13 +41,9 @@ namespace wan {
 
 namespace {
 
-#ifndef WAN_ATTN_WAVES
-#define WAN_ATTN_WAVES 4
-#endif
-#ifndef WAN_ATTN_SETPRIO
-#define WAN_ATTN_SETPRIO 0
-#endif
-constexpr int kWaves = WAN_ATTN_WAVES;
+constexpr int kWaves = 8;                    // two groups of four, one wave of each per SIMD
+constexpr int kAheadV = 4;                   // V fragments read ahead of their MFMAs
+constexpr int kAheadK = 4;                   // K fragments read ahead of their MFMAs
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
 constexpr int kHD = 128;                     // head size
@@ -52,6 +55,9 @@ constexpr float kRescaleThreshold = 8.0f;    // log2 units
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 template <int N>
 struct Int {
@@ -75,14 +81,18 @@ __device__ __forceinline__ int v_phys(int r, int ch) { return ch ^ ((r & 3) << 2
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs a) {
+// kCross only names the instantiation (self- vs cross-attention) so that
+// profiles report the two calls separately; the code is the same.
+template <int kCross>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
-  char* const Ks = smem;                    // K tiles, buffers 0 and 1
-  char* const Vs = smem + 2 * kTileBytes;   // V tiles, buffers 0 and 1
+  char* const Ks = smem;                    // K tiles, slots 0 and 1
+  char* const Vs = smem + 2 * kTileBytes;   // V tiles, slots 0 and 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int group = wave / (kWaves / 2);    // 0: leads, 1: one phase behind
   const int r32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -109,8 +119,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
 
   // Per-lane global offsets of this wave's tile loads: load i of wave w
-  // fills tile rows 4(4w + i) .. +3; lane l stores physical chunk l % 16 of
-  // row 4(4w + i) + l / 16, which holds logical chunk (l % 16) ^ swizzle.
+  // fills tile rows 4(kLoadsPerWave w + i) .. +3; lane l stores physical
+  // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, which holds logical
+  // chunk (l % 16) ^ swizzle.
   uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -120,21 +131,25 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
     vo_v[i] = r * row_v + (v_phys(r, p) << 4);
   }
   u32x4 kreg[kLoadsPerWave], vreg[kLoadsPerWave];
-  auto issue = [&](int t) {
-    const uint32_t sk = (uint32_t)t * kBN * row_k, sv = (uint32_t)t * kBN * row_v;
+  auto load_k = [&](int t) {
+    const uint32_t sk = (uint32_t)t * kBN * row_k;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k[i], sk, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_v[i], sv, 0);
-    }
+    for (int i = 0; i < kLoadsPerWave; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k[i], sk, 0);
   };
-  auto stage = [&](int buf) {
+  auto load_v = [&](int t) {
+    const uint32_t sv = (uint32_t)t * kBN * row_v;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int off = buf * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16;
-      *reinterpret_cast<u32x4*>(Ks + off) = kreg[i];
-      *reinterpret_cast<u32x4*>(Vs + off) = vreg[i];
-    }
+    for (int i = 0; i < kLoadsPerWave; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_v[i], sv, 0);
+  };
+  auto store_k = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      *reinterpret_cast<u32x4*>(Ks + slot * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16) = kreg[i];
+  };
+  auto store_v = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      *reinterpret_cast<u32x4*>(Vs + slot * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16) = vreg[i];
   };
 
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
@@ -147,13 +162,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
   }
 
   if (nT > 0) {
-    issue(0);
-    stage(0);
+    load_k(0);
+    store_k(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);   // Q and tile 0 have landed
+  __builtin_amdgcn_s_waitcnt(0);   // Q and K tile 0 have landed
   __syncthreads();
 
-  // LDS read addresses (byte offsets inside a tile; the buffer, the 32-key
+  // LDS read addresses (byte offsets inside a tile; the slot, the 32-key
   // block and the key chunk are immediate offsets).
   int ka[8];
 #pragma unroll
@@ -172,41 +187,84 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m_used = -INFINITY;
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 s[2];
+  bf16x8 pf[4];
 
-  auto body = [&](auto bufc, int t) {
-    constexpr int buf = decltype(bufc)::value;
-    if (t + 1 < nT) issue(t + 1);
-
-    // ---- S^T = K Q^T for 64 keys: two 32-key blocks x 8 dim steps.
-    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    const char* Kt = Ks + buf * kTileBytes;
-    f32x16 s[2];
+  // GEMM phase of tile jj: O^T += V^T P^T for tile jj - 1 (V slot 1 - KS),
+  // then S^T = K Q^T for tile jj (K slot KS).
+  auto gemm = [&](auto ksc, int jj) {
+    constexpr int KS = decltype(ksc)::value;
+    if (jj >= 1 && jj <= nT) {
+      const char* Vt = Vs + (1 - KS) * kTileBytes;
+      s16x4 lo[16], hi[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kc = 0; kc < 4; ++kc) {
+        const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) {
+          lo[kc * 4 + db] = lds_read_tr(Vt + va[db] + krow * kRowBytes);
+          hi[kc * 4 + db] = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
+        }
       }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const s16x8 cat =
+              __builtin_shufflevector(lo[kc * 4 + db], hi[kc * 4 + db], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, cat), pf[kc], oacc[db], 0, 0, 0);
+        }
+      }
+      // issue order: kAheadV fragments, then one MFMA per fragment read
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadV * 2, 0);
+#pragma unroll
+      for (int i = 0; i < 16 - kAheadV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadV, 0);
     }
+    if (jj < nT) {
+      const char* Kt = Ks + KS * kTileBytes;
+      bf16x8 kf[16];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kf[c * 2 + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * 2 + kb], qf[c], s[kb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadK, 0);
+#pragma unroll
+      for (int i = 0; i < 16 - kAheadK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadK, 0);
+    }
+  };
 
-    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    // ---- mask keys past kv_len (last tile only)
-    if ((t + 1) * kBN > kv_len) {
+  // Softmax phase of tile jj: running max/sum update and P = exp2(...) as bf16.
+  auto softmax = [&](int jj) {
+    if (jj < 0 || jj >= nT) return;
+    if ((jj + 1) * kBN > kv_len) {   // keys past kv_len (last tile only)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = t * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+          const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
           if (key >= kv_len) s[kb][v] = -INFINITY;
         }
     }
-
-    // ---- online softmax (log2 domain)
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
@@ -230,7 +288,6 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
       m_used = mn;
     }
     const float neg_m = -m_used;
-    bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       float p[8];
@@ -242,38 +299,52 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
       f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
       pf[kc] = __builtin_convertvector(pv, bf16x8);
     }
-
-    // ---- O^T += V^T P^T: 4 dim blocks x 4 key chunks of 16.
-    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    const char* Vt = Vs + buf * kTileBytes;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const s16x4 lo = lds_read_tr(Vt + va[db] + krow * kRowBytes);
-        const s16x4 hi = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
-        const s16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, cat), pf[kc], oacc[db], 0, 0, 0);
-      }
-    }
-
-    if (WAN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    if (t + 1 < nT) {
-      // Buffer buf ^ 1 was last read in iteration t - 1, which every wave
-      // finished before the barrier that ended it.
-      stage(buf ^ 1);
-      __syncthreads();
-    }
   };
 
-  int t = 0;
-  for (; t + 1 < nT; t += 2) {
-    body(Int<0>{}, t);
-    body(Int<1>{}, t + 1);
+  // Two groups of waves run the same phase sequence, group 1 one interval
+  // behind group 0, so that in every interval one wave of each SIMD is in a
+  // GEMM phase (MFMA) while the other is in a softmax phase (VALU):
+  //   phase 2j: GEMM(j) = PV(j-1) + S(j);   phase 2j+1: softmax(j).
+  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
+  // loads of K(j+1) and V(j) start at interval 2j and are stored at the end
+  // of interval 2j+1 into the slots freed by K(j-1) and V(j-2).
+  const int nIntervals = 2 * nT + 2;
+  for (int i = 0; i < nIntervals; i += 4) {
+    const int j0 = i >> 1;            // even tile index of this round
+    // interval i (tile j0)
+    if (j0 < nT) {
+      if (j0 + 1 < nT) load_k(j0 + 1);
+      load_v(j0);
+    }
+    if (group == 0) gemm(Int<0>{}, j0);
+    else softmax(j0 - 1);
+    __syncthreads();
+    // interval i + 1
+    if (group == 0) softmax(j0);
+    else gemm(Int<0>{}, j0);
+    if (j0 < nT) {
+      if (j0 + 1 < nT) store_k(1);
+      store_v(0);
+    }
+    __syncthreads();
+    // interval i + 2 (tile j0 + 1)
+    const int j1 = j0 + 1;
+    if (j1 < nT) {
+      if (j1 + 1 < nT) load_k(j1 + 1);
+      load_v(j1);
+    }
+    if (group == 0) gemm(Int<1>{}, j1);
+    else softmax(j0);
+    __syncthreads();
+    // interval i + 3
+    if (group == 0) softmax(j1);
+    else gemm(Int<1>{}, j1);
+    if (j1 < nT) {
+      if (j1 + 1 < nT) store_k(0);
+      store_v(1);
+    }
+    __syncthreads();
   }
-  if (t < nT) body(Int<0>{}, t);
 
   // ---- epilogue: combine the two half-waves' partial sums, normalise, store.
   float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -302,12 +373,15 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_kernel(AttnArgs
   }
 }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_fwd(const AttnArgs& a, bool cross, hipStream_t s) {
   const int nQ = (a.Lq + kBM - 1) / kBM;
   const int64_t total = (int64_t)a.B * a.H * nQ;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  if (cross)
+    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<0>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

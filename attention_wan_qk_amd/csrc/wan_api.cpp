@@ -213,7 +213,7 @@ wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k,
   a.ld_o = ld_o;
   const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  return from_hip(wan::launch_attn_fwd(a, stream));
+  return from_hip(wan::launch_attn_fwd(a, false, stream));
 }
 
 wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void* v,
@@ -246,7 +246,7 @@ wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void
   a.ld_o = ld_o;
   const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  return from_hip(wan::launch_attn_fwd(a, stream));
+  return from_hip(wan::launch_attn_fwd(a, true, stream));
 }
 
 wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x, const void* y,

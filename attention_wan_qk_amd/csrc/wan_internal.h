@@ -50,6 +50,6 @@ struct AttnArgs {
 
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_adaln(const AdaLNArgs& a, hipStream_t s);
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_fwd(const AttnArgs& a, bool cross, hipStream_t s);
 
 }  // namespace wan
