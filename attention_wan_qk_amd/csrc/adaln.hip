@@ -5,9 +5,12 @@
 // x = x + y * e[2] (gated residual) and x = x + cross_attn(norm3(x), ...)
 // (ungated residual, norm3 being the same LayerNorm with an affine).
 //
-// Memory-bound: the row is read once as 16-byte vectors, kept in fp32
-// registers (at most 16 vectors of 8 per lane), reduced twice across the
-// wave (mean, then the centred sum of squares) and written once per output.
+// Memory-bound: the row is read once as 16-byte vectors, kept in registers,
+// reduced twice across the wave (mean, then the centred sum of squares) and
+// written once per output. The kernel is specialised on whether there is a
+// residual input (without one the row stays packed bf16 and is widened on
+// each pass, which halves its registers) and on whether the normalised output
+// is wanted (without it there is nothing to reduce).
 #include "wan_device.h"
 #include "wan_internal.h"
 
@@ -20,7 +23,7 @@ __device__ __forceinline__ void load8f(const float* p, float* f) {
   f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
 }
 
-template <int NCH>
+template <int NCH, bool kY, bool kH>
 __global__ __launch_bounds__(256) void adaln_kernel(AdaLNArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -32,61 +35,87 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdaLNArgs a) {
   const float* shift = a.shift ? a.shift + moff : nullptr;
   const float* scale = a.scale ? a.scale + moff : nullptr;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + row * a.C;
-  const uint16_t* y = a.y ? static_cast<const uint16_t*>(a.y) + row * a.C : nullptr;
+  const uint16_t* y = kY ? static_cast<const uint16_t*>(a.y) + row * a.C : nullptr;
+  uint16_t* xo = a.x_out ? static_cast<uint16_t*>(a.x_out) + row * a.C : nullptr;
+  uint16_t* ho = kH ? static_cast<uint16_t*>(a.h_out) + row * a.C : nullptr;
 
   u32x4 xv[NCH], yv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + kWave * i;
     const bool in = c < nchunk;
-    xv[i] = in ? *reinterpret_cast<const u32x4*>(x + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    yv[i] = (in && y) ? *reinterpret_cast<const u32x4*>(y + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    xv[i] = in ? load_stream(x + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    if (kY) yv[i] = in ? load_stream(y + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
-  float r[NCH][8];
-  float sum = 0.f;
+
+  // r = x + gate * y in fp32 (the residual row); without y it is x itself.
+  float r[kY ? NCH : 1][8];
+  auto row_vals = [&](int i, float* f) __attribute__((always_inline)) {
+    if (kY) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = lane + kWave * i;
-    unpack8(xv[i], r[i]);
-    if (y && c < nchunk) {
-      float yf[8];
+      for (int e = 0; e < 8; ++e) f[e] = r[kY ? i : 0][e];
+    } else {
+      unpack8(xv[i], f);
+    }
+  };
+  if (kY) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + kWave * i;
+      float xf[8], yf[8];
+      unpack8(xv[i], xf);
       unpack8(yv[i], yf);
-      if (gate) {
+      if (gate && c < nchunk) {
         float g[8];
         load8f(gate + 8 * c, g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[i][e] = fmaf(g[e], yf[e], r[i][e]);
+        for (int e = 0; e < 8; ++e) r[kY ? i : 0][e] = fmaf(g[e], yf[e], xf[e]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[i][e] += yf[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sum += r[i][e];
-  }
-  const float inv_c = 1.0f / (float)a.C;
-  const float mean = wave_sum(sum) * inv_c;
-  float sq = 0.f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    if (lane + kWave * i < nchunk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = r[i][e] - mean;
-        sq = fmaf(d, d, sq);
+        for (int e = 0; e < 8; ++e) r[kY ? i : 0][e] = xf[e] + yf[e];
       }
     }
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(sq) * inv_c + a.eps);
 
-  uint16_t* xo = a.x_out ? static_cast<uint16_t*>(a.x_out) + row * a.C : nullptr;
-  uint16_t* ho = a.h_out ? static_cast<uint16_t*>(a.h_out) + row * a.C : nullptr;
+  float mean = 0.f, rstd = 0.f;
+  if (kH) {
+    const float inv_c = 1.0f / (float)a.C;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      float f[8];
+      row_vals(i, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += f[e];
+    }
+    mean = wave_sum(sum) * inv_c;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (lane + kWave * i < nchunk) {
+        float f[8];
+        row_vals(i, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = f[e] - mean;
+          sq = fmaf(d, d, sq);
+        }
+      }
+    }
+    rstd = 1.0f / sqrtf(wave_sum(sq) * inv_c + a.eps);
+  }
+  // Keep the modulation loads below the reductions: hoisting them would hold
+  // two more rows of registers and cut occupancy.
+  __builtin_amdgcn_sched_barrier(0);
+
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + kWave * i;
     if (c >= nchunk) continue;
-    if (xo) *reinterpret_cast<u32x4*>(xo + 8 * c) = pack8(r[i]);
-    if (ho) {
+    float f[8];
+    row_vals(i, f);
+    if (xo) store_stream(xo + 8 * c, kY ? pack8(f) : xv[i]);
+    if (kH) {
       float sc[8], sh[8], hv[8];
       if (scale) load8f(scale + 8 * c, sc);
       else {
@@ -99,17 +128,21 @@ __global__ __launch_bounds__(256) void adaln_kernel(AdaLNArgs a) {
         for (int e = 0; e < 8; ++e) sh[e] = 0.f;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        hv[e] = fmaf((r[i][e] - mean) * rstd, 1.0f + sc[e], sh[e]);
-      *reinterpret_cast<u32x4*>(ho + 8 * c) = pack8(hv);
+      for (int e = 0; e < 8; ++e) hv[e] = fmaf((f[e] - mean) * rstd, 1.0f + sc[e], sh[e]);
+      store_stream(ho + 8 * c, pack8(hv));
     }
+    __builtin_amdgcn_sched_barrier(0);   // one chunk's modulation vectors live at a time
   }
 }
 
 template <int NCH>
 static hipError_t launch_nch(const AdaLNArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((a.rows + 3) / 4);
-  hipLaunchKernelGGL(adaln_kernel<NCH>, dim3(blocks), dim3(256), 0, s, a);
+  const bool y = a.y != nullptr, h = a.h_out != nullptr;
+  if (y && h) hipLaunchKernelGGL((adaln_kernel<NCH, true, true>), dim3(blocks), dim3(256), 0, s, a);
+  else if (y) hipLaunchKernelGGL((adaln_kernel<NCH, true, false>), dim3(blocks), dim3(256), 0, s, a);
+  else if (h) hipLaunchKernelGGL((adaln_kernel<NCH, false, true>), dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((adaln_kernel<NCH, false, false>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ __device__ __forceinline__ void norm_rope_one(
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + kWave * i;
-    if (c < nchunk) v[i] = *reinterpret_cast<const u32x4*>(src + 8 * c);
+    if (c < nchunk) v[i] = load_stream(src + 8 * c);
     else v[i] = u32x4{0u, 0u, 0u, 0u};
   }
   float scale[NCH];
@@ -88,7 +88,7 @@ __device__ __forceinline__ void norm_rope_one(
         f[2 * p + 1] = re * sn[p] + im * cs[p];
       }
     }
-    *reinterpret_cast<u32x4*>(dst + 8 * c) = pack8(f);
+    store_stream(dst + 8 * c, pack8(f));
   }
 }
 

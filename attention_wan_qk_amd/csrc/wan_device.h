@@ -37,6 +37,15 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return __builtin_bit_cast(u32x4, b);
 }
 
+// Streaming 16-byte accesses for data touched once (nontemporal hint: the
+// activations are read and written exactly once per call).
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint16_t* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
