@@ -45,10 +45,15 @@ constexpr int kWaves = 8;                    // two groups of four, one wave of 
 constexpr int kAheadV = 4;                   // V fragments read ahead of their MFMAs
 constexpr int kAheadK = 4;                   // K fragments read ahead of their MFMAs
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
-constexpr int kBN = 64;                      // keys per tile
+#ifndef WAN_ATTN_BN
+#define WAN_ATTN_BN 64
+#endif
+constexpr int kBN = WAN_ATTN_BN;             // keys per tile
+constexpr int kKB = kBN / 32;                // 32-key blocks per tile
+constexpr int kKC = kBN / 16;                // 16-key chunks per tile (PV k-steps)
 constexpr int kHD = 128;                     // head size
 constexpr int kRowBytes = kHD * 2;
-constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB
+constexpr int kTileBytes = kBN * kRowBytes;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB per load instruction
 constexpr float kRescaleThreshold = 8.0f;    // log2 units
@@ -187,8 +192,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m_used = -INFINITY;
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
-  f32x16 s[2];
-  bf16x8 pf[4];
+  f32x16 s[kKB];
+  bf16x8 pf[kKC];
 
   // GEMM phase of tile jj: O^T += V^T P^T for tile jj - 1 (V slot 1 - KS),
   // then S^T = K Q^T for tile jj (K slot KS).
@@ -196,9 +201,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     constexpr int KS = decltype(ksc)::value;
     if (jj >= 1 && jj <= nT) {
       const char* Vt = Vs + (1 - KS) * kTileBytes;
-      s16x4 lo[16], hi[16];
+      s16x4 lo[4 * kKC], hi[4 * kKC];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < kKC; ++kc) {
         const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         }
       }
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < kKC; ++kc) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const s16x8 cat =
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       // issue order: kAheadV fragments, then one MFMA per fragment read
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadV * 2, 0);
 #pragma unroll
-      for (int i = 0; i < 16 - kAheadV; ++i) {
+      for (int i = 0; i < 4 * kKC - kAheadV; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
       }
@@ -227,25 +232,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     if (jj < nT) {
       const char* Kt = Ks + KS * kTileBytes;
-      bf16x8 kf[16];
+      bf16x8 kf[8 * kKB];
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          kf[c * 2 + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
+        for (int kb = 0; kb < kKB; ++kb)
+          kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * 2 + kb], qf[c], s[kb], 0, 0, 0);
+        for (int kb = 0; kb < kKB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * kKB + kb], qf[c], s[kb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadK, 0);
 #pragma unroll
-      for (int i = 0; i < 16 - kAheadK; ++i) {
+      for (int i = 0; i < 8 * kKB - kAheadK; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       }
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     if (jj < 0 || jj >= nT) return;
     if ((jj + 1) * kBN > kv_len) {   // keys past kv_len (last tile only)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
@@ -269,7 +274,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
+    for (int kb = 1; kb < kKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     const float neg_m = -m_used;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < kKC; ++kc) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
