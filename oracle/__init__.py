@@ -26,4 +26,6 @@ from .wan_oracle import (  # noqa: F401
     attention,
     self_attention,
     cross_attention,
+    chunk_causal_visible,
+    chunk_causal_attention,
 )

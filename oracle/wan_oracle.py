@@ -316,3 +316,58 @@ def cross_attention(q, k, v, H: int, context_lens=None, scale=None,
     model width. q: [B, Lq, H*d]; k, v: [B, Lk, H*d]. No RoPE.
     """
     return _mha(q, k, v, H, context_lens, scale, rows)
+
+
+def chunk_causal_visible(Lq: int, Lk: int, q_offset: int, chunk_len: int,
+                         k_len: int) -> np.ndarray:
+    """Visibility of key j to query i under chunk-wise autoregression, [Lq, Lk].
+
+    "Wan2.2 code walkthrough", the causalization passage (world-action models):
+    a video is generated chunk by chunk; tokens of a chunk attend to each other
+    and to every earlier (already observed or generated) chunk, never to a
+    later one. Query i sits at global position q_offset + i (the newest chunk
+    after a cache of earlier keys); key j at position j; chunk(x) =
+    floor(x / chunk_len). Key j is visible iff j < k_len and
+    chunk(j) <= chunk(q_offset + i).
+    """
+    qi = q_offset + np.arange(Lq)[:, None]
+    kj = np.arange(Lk)[None, :]
+    return (kj < k_len) & (kj // chunk_len <= qi // chunk_len)
+
+
+def chunk_causal_attention(q, k, v, H: int, q_offset: int, chunk_len: int,
+                           k_lens=None, scale=None, rows=None):
+    """Self-attention with the chunk-causal visibility above, per (b, h).
+
+    q: [B, Lq, H*d] (the newest tokens), k, v: [B, Lk, H*d] (cache + newest).
+    Returns o [B, rows, H*d] and lse [B, H, rows]; a row with no visible key
+    gets o = 0, lse = -inf.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Lq, C = q.shape
+    Lk = k.shape[1]
+    d = C // H
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, rows.size, C))
+    lse = np.full((B, H, rows.size), -np.inf)
+    for b in range(B):
+        kl = Lk if k_lens is None else int(k_lens[b])
+        vis = chunk_causal_visible(Lq, Lk, q_offset, chunk_len, kl)[rows]
+        for hh in range(H):
+            sl = slice(hh * d, (hh + 1) * d)
+            qq = _f64(q[b, rows, sl])
+            kk = _f64(k[b, :, sl])
+            vv = _f64(v[b, :, sl])
+            s = np.where(vis, (qq @ kk.T) * scale, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            ok = np.isfinite(m[:, 0])
+            p = np.where(vis, np.exp(s - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            l = p.sum(axis=1, keepdims=True)
+            o[b, ok, sl] = (p[ok] @ vv) / l[ok]
+            lse[b, hh, ok] = (m[ok] + np.log(l[ok]))[:, 0]
+    return o, lse
+

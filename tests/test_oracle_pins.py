@@ -403,3 +403,50 @@ def test_qk_norm_rope3d_row_subset_equals_full():
     rows = np.array([0, 7, 33, 59])
     sub = O.qk_norm_rope3d(x[:, rows], g, grid, H, rows=rows)
     assert np.array_equal(sub, full[:, rows])
+
+
+# ------------------------------------------------------- chunk-causal ----
+def test_chunk_causal_with_one_chunk_is_full_attention():
+    B, L, H, d = 2, 37, 2, 16
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    kl = np.array([37, 20])
+    full, fl = O.self_attention(q, k, v, H, kl)
+    cc, cl = O.chunk_causal_attention(q, k, v, H, 0, 1000, kl)
+    assert np.allclose(cc, full, atol=1e-12) and np.allclose(cl, fl, atol=1e-12)
+
+
+def test_chunk_causal_with_unit_chunks_is_torch_causal():
+    L, d = 29, 16
+    q, k, v = RNG.standard_normal((3, 1, L, d))
+    cc, _ = O.chunk_causal_attention(q, k, v, 1, 0, 1)
+    want = F.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None], torch.from_numpy(k)[:, None],
+        torch.from_numpy(v)[:, None], is_causal=True).numpy()[:, 0]
+    assert np.allclose(cc, want, atol=1e-12)
+
+
+def test_chunk_causal_visibility_brute_force_and_cache_offset():
+    Lq, Lk, off, cl = 6, 14, 8, 4
+    vis = O.chunk_causal_visible(Lq, Lk, off, cl, 13)
+    for i in range(Lq):
+        for j in range(Lk):
+            assert vis[i, j] == (j < 13 and (j // cl) <= ((off + i) // cl))
+    # newest tokens attending to a cache: equal to the matching rows of the
+    # whole sequence computed at once
+    B, H, d = 1, 2, 16
+    q, k, v = RNG.standard_normal((3, B, Lk, H * d))
+    whole, _ = O.chunk_causal_attention(q, k, v, H, 0, cl)
+    tail, _ = O.chunk_causal_attention(q[:, off:], k, v, H, off, cl)
+    assert np.allclose(tail, whole[:, off:], atol=1e-12)
+
+
+def test_chunk_causal_future_chunks_have_no_effect():
+    B, L, H, d, cl = 1, 40, 1, 16, 8
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    o1, _ = O.chunk_causal_attention(q, k, v, H, 0, cl)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 24:] = 50 * RNG.standard_normal((B, 16, d))
+    v2[:, 24:] = 1e3
+    o2, _ = O.chunk_causal_attention(q, k2, v2, H, 0, cl)
+    assert np.array_equal(o1[:, :24], o2[:, :24])      # chunks 0..2 never see 3, 4
+    assert not np.allclose(o1[:, 24:], o2[:, 24:])
