@@ -33,6 +33,8 @@ SIGNATURES = {
                                _F, _P]),
     "wan_cross_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _L, _F,
                                 _P]),
+    "wan_chunk_causal_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       _L, _L, _L, _L, _F, _P]),
     "wan_adaln_modulate_gate": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _F,
                                      _P]),
 }

@@ -86,9 +86,9 @@ __device__ __forceinline__ int v_phys(int r, int ch) { return ch ^ ((r & 3) << 2
 
 }  // namespace
 
-// kCross only names the instantiation (self- vs cross-attention) so that
-// profiles report the two calls separately; the code is the same.
-template <int kCross>
+// kKind: 0 self-attention, 1 cross-attention (same code; separate names in
+// profiles), 2 chunk-causal self-attention (per-row key limit, see below).
+template <int kKind>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
   char* const Ks = smem;                    // K tiles, slots 0 and 1
@@ -111,7 +111,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
   int kv_len = a.Lk;
   if (a.k_lens) kv_len = min(max(a.k_lens[b], 0), a.Lk);
-  const int nT = (kv_len + kBN - 1) / kBN;
+  // Chunk-causal: query row r (global position q_offset + r) sees keys below
+  // min(kv_len, (chunk(q_offset + r) + 1) * chunk_len). The workgroup streams
+  // the tiles its last row needs and masks per row beyond its first row's limit.
+  constexpr bool kCausal = kKind == 2;
+  auto key_limit = [&](int row) {
+    if (!kCausal) return kv_len;
+    const int64_t c = ((int64_t)a.q_offset + row) / a.chunk_len + 1;
+    return (int)min((int64_t)kv_len, c * a.chunk_len);
+  };
+  const int lim_lo = key_limit(min(qt * kBM, a.Lq - 1));
+  const int lim_hi = key_limit(min(qt * kBM + kBM - 1, a.Lq - 1));
+  const int nT = (lim_hi + kBN - 1) / kBN;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.Lq * a.ld_q + h * kHD;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)b * a.Lk * a.ld_k + h * kHD;
@@ -159,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
   const int qrow = qt * kBM + wave * 32 + r32;
+  const int lim_row = key_limit(min(qrow, a.Lq - 1));
   bf16x8 qf[8];
   {
     const uint16_t* qr = qg + (int64_t)min(qrow, a.Lq - 1) * a.ld_q + 8 * hf;
@@ -261,13 +273,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   // Softmax phase of tile jj: running max/sum update and P = exp2(...) as bf16.
   auto softmax = [&](int jj) {
     if (jj < 0 || jj >= nT) return;
-    if ((jj + 1) * kBN > kv_len) {   // keys past kv_len (last tile only)
+    if ((jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (key >= kv_len) s[kb][v] = -INFINITY;
+          if (key >= lim_row) s[kb][v] = -INFINITY;
         }
     }
     float mx = fmaxf(s[0][0], s[0][1]);
@@ -380,15 +392,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, bool cross, hipStream_t s) {
+hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s) {
   const int nQ = (a.Lq + kBM - 1) / kBM;
   const int64_t total = (int64_t)a.B * a.H * nQ;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  if (cross)
-    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<0>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  const dim3 grid((unsigned)total), block(kThreads);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(attn_fwd_kernel<0>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL(attn_fwd_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(attn_fwd_kernel<2>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

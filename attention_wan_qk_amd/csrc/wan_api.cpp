@@ -213,7 +213,9 @@ wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k,
   a.ld_o = ld_o;
   const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  return from_hip(wan::launch_attn_fwd(a, false, stream));
+  a.q_offset = 0;
+  a.chunk_len = 0;
+  return from_hip(wan::launch_attn_fwd(a, 0, stream));
 }
 
 wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void* v,
@@ -246,7 +248,44 @@ wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void
   a.ld_o = ld_o;
   const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  return from_hip(wan::launch_attn_fwd(a, true, stream));
+  a.q_offset = 0;
+  a.chunk_len = 0;
+  return from_hip(wan::launch_attn_fwd(a, 1, stream));
+}
+
+wanStatus_t wan_chunk_causal_attn_fwd(void* o, float* lse, const void* q, const void* k,
+                                      const void* v, const int32_t* k_lens, int B, int Lq,
+                                      int Lk, int H, int D, int q_offset, int chunk_len,
+                                      int64_t ld_q, int64_t ld_k, int64_t ld_v, int64_t ld_o,
+                                      float softmax_scale, hipStream_t stream) {
+  if (B < 0 || Lq < 0 || Lk < 1 || q_offset < 0 || chunk_len < 1) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * Lq == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  wanStatus_t st = check_attn(o, lse, q, k, v, B, Lq, Lk, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  wan::AttnArgs a;
+  a.o = o;
+  a.lse = lse;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_lens = k_lens;
+  a.B = B;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.H = H;
+  a.ld_q = ld_q;
+  a.ld_k = ld_k;
+  a.ld_v = ld_v;
+  a.ld_o = ld_o;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.q_offset = q_offset;
+  a.chunk_len = chunk_len;
+  return from_hip(wan::launch_attn_fwd(a, 2, stream));
 }
 
 wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x, const void* y,

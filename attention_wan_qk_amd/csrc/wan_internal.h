@@ -46,10 +46,13 @@ struct AttnArgs {
   int B, Lq, Lk, H;
   int64_t ld_q, ld_k, ld_v, ld_o;
   float scale_log2;   // softmax scale * log2(e)
+  int q_offset;       // chunk-causal only: global position of query row 0
+  int chunk_len;      // chunk-causal only: tokens per chunk (>= 1)
 };
 
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_adaln(const AdaLNArgs& a, hipStream_t s);
-hipError_t launch_attn_fwd(const AttnArgs& a, bool cross, hipStream_t s);
+// kind: 0 self-attention, 1 cross-attention, 2 chunk-causal self-attention.
+hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s);
 
 }  // namespace wan

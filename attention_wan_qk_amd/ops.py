@@ -119,6 +119,27 @@ def cross_attn_fwd(q, k, v, heads: int, context_lens=None, scale: float = 0.0, o
     return out
 
 
+def chunk_causal_attn_fwd(q, k, v, heads: int, q_offset: int, chunk_len: int, k_lens=None,
+                          scale: float = 0.0, out=None, return_lse: bool = False):
+    """Self-attention of q [B, Lq, C] (tokens q_offset ..) over k, v [B, Lk, C]
+    where a key is visible iff its chunk is not after the query's chunk."""
+    C = _channels(q)
+    B, Lq, ld_q = _token_major(q, "q", C)
+    _, Lk, ld_k = _token_major(k, "k", C)
+    _, _, ld_v = _token_major(v, "v", C)
+    if out is None:
+        out = torch.empty(B, Lq, C, dtype=torch.bfloat16, device=q.device)
+    ld_o = _token_major(out, "out", C)[2]
+    lse = torch.empty(B, heads, Lq, dtype=torch.float32, device=q.device) if return_lse else None
+    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
+        raise TypeError("k_lens must be a CUDA int32 tensor")
+    st = lib().wan_chunk_causal_attn_fwd(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(k_lens), B, Lq, Lk, heads, C // heads, q_offset,
+                                         chunk_len, ld_q, ld_k, ld_v, ld_o, scale, _stream(q))
+    check("wan_chunk_causal_attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
 def _mod_strides(vecs, B, L, C):
     strides = None
     for v in vecs:

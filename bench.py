@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the oracle sample on the host")
+    p.add_argument("--chunk-frames", type=int, default=0,
+                   help="also time chunk-causal self-attention with chunks of this many "
+                        "latent frames (stderr only)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one device copy of this many MiB (a kernel of known "
                         "traffic, to scale HBM byte counters)")
@@ -104,6 +107,32 @@ def cpu_baseline(w, tensors, budget_s: float):
         "sample": f"self-attention of {len(rows)} query rows x {pairs} (batch, head) pairs of "
                   f"{w.name} (L={w.tokens}), float64 NumPy, {dt:.1f} s incl. host copies",
     }
+
+
+def breakdown_causal(args, w, ops, q, k, v, o, full_ms):
+    """Time wan_chunk_causal_attn_fwd over the whole clip with chunks of
+    ``--chunk-frames`` latent frames; FLOPs count only visible (query, key)
+    pairs: 4 d H B sum_i keys_visible(i)."""
+    import torch
+    L, H = w.tokens, w.heads
+    chunk = args.chunk_frames * w.grid[1] * w.grid[2]
+    pairs = sum(min(chunk, L - c0) * min(L, c0 + chunk) for c0 in range(0, L, chunk))
+    flop = 4.0 * w.head_dim * H * w.batch * pairs
+    for _ in range(args.warmup):
+        ops.chunk_causal_attn_fwd(q, k, v, H, 0, chunk, out=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(args.steps):
+        ops.chunk_causal_attn_fwd(q, k, v, H, 0, chunk, out=o)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    tf = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({"chunk_causal": {
+        "chunk_frames": args.chunk_frames, "chunk_tokens": chunk,
+        "visible_fraction": round(pairs / (L * L), 4), "ms": round(ms, 4),
+        "tflops_visible": round(tf, 1), "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "time_vs_full": round(ms / full_ms, 4)}}), file=sys.stderr, flush=True)
 
 
 def main():
@@ -207,6 +236,9 @@ def main():
             rec.update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
         breakdown[n] = rec
     print(json.dumps({"breakdown": breakdown}), file=sys.stderr, flush=True)
+
+    if args.chunk_frames > 0:
+        breakdown_causal(args, w, ops, qr, kr, t["v"], o, per["self_attn"])
 
     traffic = measured_traffic("attn_fwd_kernel", w.name)
     result = {

@@ -163,6 +163,41 @@ wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k,
                                float softmax_scale, hipStream_t stream);
 
 /*
+ * wan_chunk_causal_attn_fwd: self-attention under chunk-wise autoregression.
+ *
+ * Passage: the causalization discussion of the "Wan2.2 code walkthrough" page
+ * (turning the bidirectional video denoiser into a world model): the video is
+ * generated chunk by chunk, tokens of the chunk being denoised attend to each
+ * other and to the chunks already observed or generated (a KV cache), never to
+ * later ones.
+ *
+ * Query row i is the token at global position q_offset + i; key j is at
+ * position j; chunk(x) = floor(x / chunk_len). Key j is visible to row i iff
+ *   j < n_b  and  chunk(j) <= chunk(q_offset + i),   n_b = clamp(k_lens[b], 0, Lk).
+ * o and lse as in wan_self_attn_fwd over the visible keys (no visible key:
+ * o = 0, lse = -inf). Tiles of keys no row of a workgroup can see are skipped,
+ * so a full causal pass costs about half of full attention.
+ * chunk_len >= Lk + q_offset + Lq gives full attention; chunk_len = 1 with
+ * q_offset = 0 gives token-causal attention. Typical use: q_offset = Lk - Lq
+ * (the newest Lq tokens against cache + themselves), chunk_len = tokens of a
+ * chunk of latent frames (frames * h * w).
+ *
+ * o      bf16 [B, Lq, H, D], row stride ld_o; must not overlap q, k or v.
+ * lse    fp32 [B, H, Lq] or NULL.
+ * q      bf16 [B, Lq, H, D], row stride ld_q.
+ * k, v   bf16 [B, Lk, H, D], row strides ld_k, ld_v.
+ * Errors: as wan_self_attn_fwd; Lk >= 1, q_offset >= 0 and chunk_len >= 1
+ * are required (WAN_ERROR_INVALID_VALUE otherwise).
+ */
+wanStatus_t wan_chunk_causal_attn_fwd(void* o, float* lse, const void* q,
+                                      const void* k, const void* v,
+                                      const int32_t* k_lens, int B, int Lq,
+                                      int Lk, int H, int D, int q_offset,
+                                      int chunk_len, int64_t ld_q,
+                                      int64_t ld_k, int64_t ld_v, int64_t ld_o,
+                                      float softmax_scale, hipStream_t stream);
+
+/*
  * wan_adaln_modulate_gate: residual update + AdaLN-modulated LayerNorm.
  *
  * Passage: the WanAttentionBlock snippet of the "Wan2.2 code walkthrough" page:

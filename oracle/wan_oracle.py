@@ -319,7 +319,7 @@ def cross_attention(q, k, v, H: int, context_lens=None, scale=None,
 
 
 def chunk_causal_visible(Lq: int, Lk: int, q_offset: int, chunk_len: int,
-                         k_len: int) -> np.ndarray:
+                         k_len: int, rows=None) -> np.ndarray:
     """Visibility of key j to query i under chunk-wise autoregression, [Lq, Lk].
 
     "Wan2.2 code walkthrough", the causalization passage (world-action models):
@@ -328,9 +328,11 @@ def chunk_causal_visible(Lq: int, Lk: int, q_offset: int, chunk_len: int,
     later one. Query i sits at global position q_offset + i (the newest chunk
     after a cache of earlier keys); key j at position j; chunk(x) =
     floor(x / chunk_len). Key j is visible iff j < k_len and
-    chunk(j) <= chunk(q_offset + i).
+    chunk(j) <= chunk(q_offset + i). Returns the rows ``rows`` (default all)
+    of the [Lq, Lk] matrix.
     """
-    qi = q_offset + np.arange(Lq)[:, None]
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    qi = q_offset + rows[:, None]
     kj = np.arange(Lk)[None, :]
     return (kj < k_len) & (kj // chunk_len <= qi // chunk_len)
 
@@ -356,7 +358,7 @@ def chunk_causal_attention(q, k, v, H: int, q_offset: int, chunk_len: int,
     lse = np.full((B, H, rows.size), -np.inf)
     for b in range(B):
         kl = Lk if k_lens is None else int(k_lens[b])
-        vis = chunk_causal_visible(Lq, Lk, q_offset, chunk_len, kl)[rows]
+        vis = chunk_causal_visible(Lq, Lk, q_offset, chunk_len, kl, rows)
         for hh in range(H):
             sl = slice(hh * d, (hh + 1) * d)
             qq = _f64(q[b, rows, sl])

@@ -157,3 +157,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_chunk_causal_rejections(L):
+    def cc(**kw):
+        a = dict(o=A, lse=None, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, kl=None, B=1, Lq=64, Lk=96,
+                 H=2, D=128, off=32, cl=16, lq=0, lk=0, lv=0, lo=0, scale=0.0)
+        a.update(kw)
+        return L.wan_chunk_causal_attn_fwd(a["o"], a["lse"], a["q"], a["k"], a["v"], a["kl"],
+                                           a["B"], a["Lq"], a["Lk"], a["H"], a["D"], a["off"],
+                                           a["cl"], a["lq"], a["lk"], a["lv"], a["lo"],
+                                           a["scale"], None)
+    assert cc(cl=0) == INV
+    assert cc(off=-1) == INV
+    assert cc(Lk=0) == INV
+    assert cc(D=64) == NS
+    assert cc(o=A + MB) == INV
+    assert cc(Lq=0) == OK

@@ -450,3 +450,16 @@ def test_chunk_causal_future_chunks_have_no_effect():
     o2, _ = O.chunk_causal_attention(q, k2, v2, H, 0, cl)
     assert np.array_equal(o1[:, :24], o2[:, :24])      # chunks 0..2 never see 3, 4
     assert not np.allclose(o1[:, 24:], o2[:, 24:])
+
+
+def test_chunk_causal_row_subset_equals_full():
+    B, Lq, Lk, H, d, off, cl = 2, 23, 50, 2, 16, 27, 10
+    q = RNG.standard_normal((B, Lq, H * d))
+    k, v = RNG.standard_normal((2, B, Lk, H * d))
+    kl = np.array([50, 31])
+    full, fl = O.chunk_causal_attention(q, k, v, H, off, cl, kl)
+    rows = np.array([0, 2, 3, 12, 22])
+    sub, sl = O.chunk_causal_attention(q, k, v, H, off, cl, kl, rows=rows)
+    assert np.array_equal(sub, full[:, rows]) and np.array_equal(sl, fl[:, :, rows])
+    assert np.array_equal(O.chunk_causal_visible(Lq, Lk, off, cl, 31, rows),
+                          O.chunk_causal_visible(Lq, Lk, off, cl, 31)[rows])
