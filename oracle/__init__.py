@@ -28,4 +28,5 @@ from .wan_oracle import (  # noqa: F401
     cross_attention,
     chunk_causal_visible,
     chunk_causal_attention,
+    linear,
 )

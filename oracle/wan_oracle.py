@@ -373,3 +373,23 @@ def chunk_causal_attention(q, k, v, H: int, q_offset: int, chunk_len: int,
             lse[b, hh, ok] = (m[ok] + np.log(l[ok]))[:, 0]
     return o, lse
 
+
+
+# ----------------------------------------------------------------------------
+# Projections (the Linear layers around the attention calls)
+# ----------------------------------------------------------------------------
+def linear(x, w, bias=None) -> np.ndarray:
+    """y = x W^T + b, as a torch ``nn.Linear`` computes it.
+
+    "Wan2.2 code walkthrough", the WanModel snippet: the model's projections
+    are ``nn.Linear`` layers (weight [out, in], bias [out]); the q, k, v and
+    o projections of self- and cross-attention are Linear layers of width
+    dim. "论文专题讲解：Wan2.1", section "大规模训练系统": their cost is the
+    alpha * b * s * h^2 term next to attention's beta * b * s^2 * h.
+
+    x: [..., K]; w: [N, K]; bias: [N] or None. Returns float64 [..., N].
+    """
+    y = _f64(x) @ _f64(w).T
+    if bias is not None:
+        y = y + _f64(bias)
+    return y

@@ -463,3 +463,37 @@ def test_chunk_causal_row_subset_equals_full():
     assert np.array_equal(sub, full[:, rows]) and np.array_equal(sl, fl[:, :, rows])
     assert np.array_equal(O.chunk_causal_visible(Lq, Lk, off, cl, 31, rows),
                           O.chunk_causal_visible(Lq, Lk, off, cl, 31)[rows])
+
+
+# ---------------------------------------------------------------- linear ----
+def test_linear_brute_force_loops():
+    M, N, K = 3, 5, 7
+    x = RNG.standard_normal((M, K))
+    w = RNG.standard_normal((N, K))
+    b = RNG.standard_normal(N)
+    y = O.linear(x, w, b)
+    for m in range(M):
+        for n in range(N):
+            acc = b[n]
+            for k in range(K):
+                acc += x[m, k] * w[n, k]
+            assert abs(y[m, n] - acc) < 1e-12
+
+
+def test_linear_special_cases_and_torch():
+    x = RNG.standard_normal((2, 9, 16))
+    eye = np.eye(16)
+    assert np.array_equal(O.linear(x, eye), x)                     # identity weight
+    b = RNG.standard_normal(4)
+    assert np.array_equal(O.linear(x, np.zeros((4, 16)), b), np.broadcast_to(b, (2, 9, 4)))
+    w = RNG.standard_normal((12, 16))
+    want = F.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b.repeat(3))).numpy()
+    assert np.allclose(O.linear(x, w, b.repeat(3)), want, atol=1e-12)
+    # a fused [Wq; Wk; Wv] weight gives the three projections side by side
+    ws = np.split(w, 3)
+    parts = np.concatenate([O.linear(x, wi) for wi in ws], axis=-1)
+    assert np.allclose(O.linear(x, w), parts, atol=1e-12)
+    # bf16 bit patterns are widened exactly: 1.0 = 0x3f80, 2.0 = 0x4000
+    xb = np.array([[0x3F80, 0x4000]], dtype=np.uint16)
+    wb = np.array([[0x4000, 0x3F80]], dtype=np.uint16)
+    assert O.linear(xb, wb)[0, 0] == 4.0
