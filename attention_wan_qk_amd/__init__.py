@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     adaln_modulate_gate,
     chunk_causal_attn_fwd,
     cross_attn_fwd,
+    linear_fwd,
     qk_norm_rope3d,
     self_attn_fwd,
 )

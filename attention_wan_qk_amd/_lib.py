@@ -37,6 +37,7 @@ SIGNATURES = {
                                        _L, _L, _L, _L, _F, _P]),
     "wan_adaln_modulate_gate": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _F,
                                      _P]),
+    "wan_linear_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _P]),
 }
 
 _lib = None

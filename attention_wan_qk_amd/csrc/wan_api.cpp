@@ -332,4 +332,31 @@ wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x, con
   return from_hip(wan::launch_adaln(a, stream));
 }
 
+wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w, const float* bias, int M,
+                          int N, int K, int64_t ld_x, int64_t ld_w, int64_t ld_y,
+                          hipStream_t stream) {
+  if (M < 0 || N < 1 || K < 1) return WAN_ERROR_INVALID_VALUE;
+  if (M == 0) return WAN_SUCCESS;
+  if (!y || !x || !w) return WAN_ERROR_INVALID_VALUE;
+  if (!aligned16(y) || !aligned16(x) || !aligned16(w) || (bias && !aligned16(bias)))
+    return WAN_ERROR_INVALID_VALUE;
+  if ((N & 7) || (K & 7)) return WAN_ERROR_INVALID_VALUE;
+  if (ld_x == 0) ld_x = K;
+  if (ld_w == 0) ld_w = K;
+  if (ld_y == 0) ld_y = N;
+  if (ld_x < K || ld_w < K || ld_y < N || ((ld_x | ld_w | ld_y) & 7))
+    return WAN_ERROR_INVALID_VALUE;
+  // 256 rows of x or W must fit one 32-bit buffer range.
+  if (256 * (ld_x > ld_w ? ld_x : ld_w) * 2 > (int64_t)0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
+  const Range ry = span_bf16(y, M, ld_y, N);
+  if (overlap(ry, span_bf16(x, M, ld_x, K)) || overlap(ry, span_bf16(w, N, ld_w, K)))
+    return WAN_ERROR_INVALID_VALUE;
+  if (bias) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(bias);
+    if (overlap(ry, Range{lo, lo + (uintptr_t)N * 4})) return WAN_ERROR_INVALID_VALUE;
+  }
+  wan::LinearArgs a{y, x, w, bias, M, N, K, ld_x, ld_w, ld_y};
+  return from_hip(wan::launch_linear(a, stream));
+}
+
 }  // extern "C"

@@ -50,9 +50,19 @@ struct AttnArgs {
   int chunk_len;      // chunk-causal only: tokens per chunk (>= 1)
 };
 
+struct LinearArgs {
+  void* y;
+  const void* x;
+  const void* w;
+  const float* bias;
+  int M, N, K;
+  int64_t ld_x, ld_w, ld_y;
+};
+
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_adaln(const AdaLNArgs& a, hipStream_t s);
 // kind: 0 self-attention, 1 cross-attention, 2 chunk-causal self-attention.
 hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s);
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
 }  // namespace wan

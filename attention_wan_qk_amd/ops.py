@@ -177,3 +177,47 @@ def adaln_modulate_gate(x, y=None, gate=None, shift=None, scale=None, eps: float
                                        _stream(x))
     check("wan_adaln_modulate_gate", st)
     return x_out, h_out
+
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Stride between consecutive rows of t [..., W] whose leading dims
+    flatten to equally spaced rows."""
+    W = t.shape[-1]
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: expected unit stride in the last dim")
+    ld = t.stride(-2) if t.dim() > 1 and t.shape[-2] > 1 else W
+    exp = ld
+    for d in range(t.dim() - 2, -1, -1):
+        if t.shape[d] > 1 and t.stride(d) != exp:
+            raise ValueError(f"{name}: rows must be equally spaced")
+        exp *= t.shape[d]
+    return max(ld, W)
+
+
+def linear_fwd(x, weight, bias=None, out=None):
+    """y = x W^T + b for x [..., K] (rows may be a column slice of a wider
+    buffer), weight [N, K] bf16, bias fp32 [N] or None; returns y [..., N]."""
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("x and weight must be bf16 CUDA tensors")
+    K = x.shape[-1]
+    N = weight.shape[0]
+    if weight.dim() != 2 or weight.shape[1] != K or weight.stride(1) != 1:
+        raise ValueError("weight must be [N, K] with unit column stride")
+    lead = x.shape[:-1]
+    M = 1
+    for n in lead:
+        M *= n
+    ld_x = _row_stride(x, "x")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or
+                             not bias.is_contiguous()):
+        raise ValueError("bias must be contiguous fp32 [N]")
+    if out is None:
+        out = torch.empty(*lead, N, dtype=torch.bfloat16, device=x.device)
+    if tuple(out.shape) != (*lead, N) or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 [..., N] matching x")
+    ld_y = _row_stride(out, "out")
+    st = lib().wan_linear_fwd(_ptr(out), _ptr(x), _ptr(weight), _ptr(bias), M, N, K, ld_x,
+                              weight.stride(0), ld_y, _stream(x))
+    check("wan_linear_fwd", st)
+    return out

@@ -8,6 +8,10 @@ Recipe (per workload, every tensor from its own seed):
   cross_q, cross_y     bf16 [B, L, C]   ~ N(0, 1)
   gain_q, gain_k       fp32 [C]         ~ 1 + 0.1 N(0, 1)
   modulation e         fp32 [B, 6, C]   ~ N(0, 0.1)  (variance 0.1)
+  projection weights   bf16 [N, C]      ~ N(0, 1/C)  (q/k/v fused [3C, C], o, cross q, cross
+                                                      k/v fused [2C, C], cross o)
+  projection biases    fp32 [N]         ~ N(0, 1/C)
+  text context         bf16 [B, Lt, C]  ~ N(0, 1)
 Values are drawn in fp32 and rounded to bf16 (nearest even) by torch.
 Independent draws per batch entry, so the two CFG halves differ.
 """
@@ -20,7 +24,9 @@ import torch
 TAGS = {
     "x": 1, "y": 2, "q": 3, "k": 4, "v": 5, "text_k": 6, "text_v": 7,
     "cross_q": 8, "cross_y": 9, "gain_q": 10, "gain_k": 11, "mod": 12,
-    "gain_cq": 13, "gain_ck": 14, "rows": 99,
+    "gain_cq": 13, "gain_ck": 14, "w_qkv": 15, "b_qkv": 16, "w_o": 17, "b_o": 18,
+    "w_cq": 19, "b_cq": 20, "w_ckv": 21, "b_ckv": 22, "w_co": 23, "b_co": 24, "context": 25,
+    "rows": 99,
 }
 
 
@@ -50,6 +56,14 @@ def tensor(w, tag: str, device, salt: int = 0) -> torch.Tensor:
         return normal((B, Lt, C), s, device)
     if tag in ("gain_q", "gain_k", "gain_cq", "gain_ck"):
         return normal((C,), s, device, std=0.1, mean=1.0, dtype=torch.float32)
+    if tag in ("w_qkv", "w_o", "w_cq", "w_ckv", "w_co"):
+        rows = {"w_qkv": 3 * C, "w_ckv": 2 * C}.get(tag, C)
+        return normal((rows, C), s, device, std=C ** -0.5)
+    if tag in ("b_qkv", "b_o", "b_cq", "b_ckv", "b_co"):
+        n = {"b_qkv": 3 * C, "b_ckv": 2 * C}.get(tag, C)
+        return normal((n,), s, device, std=C ** -0.5, dtype=torch.float32)
+    if tag == "context":
+        return normal((B, Lt, C), s, device)
     if tag == "mod":
         return normal((B, 6, C), s, device, std=0.1 ** 0.5, dtype=torch.float32)
     raise KeyError(tag)

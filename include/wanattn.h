@@ -14,7 +14,9 @@
  * (section "Video DiT 与 Flow Matching": full spatio-temporal self-attention,
  * cross-attention to the 512-token umT5 text context).
  *
- * The q/k/v and output projections between the calls are the caller's.
+ * wan_linear_fwd computes the q/k/v and output projections between them
+ * (bf16 Linear layers); wan_chunk_causal_attn_fwd is the chunk-wise
+ * autoregressive variant of the self-attention.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -232,6 +234,35 @@ wanStatus_t wan_adaln_modulate_gate(void* x_out, void* h_out, const void* x,
                                     int B, int L, int C, int64_t mod_stride_b,
                                     int64_t mod_stride_l, float eps,
                                     hipStream_t stream);
+
+/*
+ * wan_linear_fwd: projection y = x W^T + b (a torch nn.Linear in bf16).
+ *
+ * Passage: the WanModel snippet of the "Wan2.2 code walkthrough" page builds
+ * the model from nn.Linear layers (weight [out, in], bias [out]); the q, k, v
+ * and o projections of self- and cross-attention are such layers of width
+ * dim. "论文专题讲解：Wan2.1", section "大规模训练系统", gives their cost as the
+ * alpha * b * s * h^2 term beside attention's beta * b * s^2 * h.
+ *
+ *   y[m, n] = bf16( sum_k x[m, k] * w[n, k] + bias[n] )
+ * with bf16 MFMA products, fp32 accumulation, the bias added in fp32 and one
+ * round to nearest even.
+ *
+ * y     bf16 [M, N], row stride ld_y (e.g. the q, k, v thirds of a fused
+ *       [M, 3C] buffer: pass N = 3C with W = [Wq; Wk; Wv], or one slice).
+ *       Must not overlap x, w or bias.
+ * x     bf16 [M, K], row stride ld_x (tokens: M = B * L).
+ * w     bf16 [N, K], row stride ld_w.
+ * bias  fp32 [N] or NULL (no bias).
+ * N and K must be multiples of 8; ld = 0 means the dense stride.
+ * Errors: WAN_ERROR_INVALID_VALUE for NULL/misaligned pointers, bad sizes or
+ * strides, y overlapping an input; WAN_ERROR_NOT_SUPPORTED when 256 rows of
+ * x or w span more than 2^31 bytes.
+ */
+wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
+                           const float* bias, int M, int N, int K,
+                           int64_t ld_x, int64_t ld_w, int64_t ld_y,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,10 +32,11 @@ def declared_calls():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(wan_\w+)\s*\(", src, re.M)))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_every_call():
     calls = declared_calls()
     for name in ("wan_qk_norm_rope3d", "wan_self_attn_fwd", "wan_cross_attn_fwd",
-                 "wan_adaln_modulate_gate", "wan_status_string", "wan_version"):
+                 "wan_adaln_modulate_gate", "wan_chunk_causal_attn_fwd", "wan_linear_fwd",
+                 "wan_status_string", "wan_version"):
         assert name in calls
 
 
@@ -174,3 +175,25 @@ def test_chunk_causal_rejections(L):
     assert cc(D=64) == NS
     assert cc(o=A + MB) == INV
     assert cc(Lq=0) == OK
+
+
+def test_linear_rejections(L):
+    def lin(**kw):
+        a = dict(y=A, x=A + MB, w=A + 2 * MB, b=None, M=300, N=264, K=200, lx=0, lw=0, ly=0)
+        a.update(kw)
+        return L.wan_linear_fwd(a["y"], a["x"], a["w"], a["b"], a["M"], a["N"], a["K"],
+                                a["lx"], a["lw"], a["ly"], None)
+    assert lin(M=0) == OK
+    assert lin(M=-1) == INV
+    assert lin(N=0) == INV
+    assert lin(K=0) == INV
+    assert lin(N=260) == INV           # N not a multiple of 8
+    assert lin(K=204) == INV           # K not a multiple of 8
+    assert lin(lx=192) == INV          # ld_x < K
+    assert lin(lw=208, ly=260) == INV  # ld_y not a multiple of 8
+    assert lin(x=None) == INV
+    assert lin(y=A + 8) == INV         # misaligned
+    assert lin(b=A + 2 * MB + 4) == INV
+    assert lin(y=A + MB + 16) == INV   # y overlaps x
+    assert lin(b=A + 16) == INV        # bias inside y
+    assert lin(lx=1 << 23) == NS       # 256 rows exceed a 32-bit buffer range
