@@ -12,6 +12,9 @@ Recipe (per workload, every tensor from its own seed):
                                                       k/v fused [2C, C], cross o)
   projection biases    fp32 [N]         ~ N(0, 1/C)
   text context         bf16 [B, Lt, C]  ~ N(0, 1)
+  image context        bf16 [B, 257, C] ~ N(0, 1)   (image tokens of the I2V decoupled
+                                                      cross-attention; count is a reading)
+  FFN output           bf16 [B, L, C]   ~ N(0, 1)   (stands in for ffn(h2) at the e5 gate)
 Values are drawn in fp32 and rounded to bf16 (nearest even) by torch.
 Independent draws per batch entry, so the two CFG halves differ.
 """
@@ -26,8 +29,12 @@ TAGS = {
     "cross_q": 8, "cross_y": 9, "gain_q": 10, "gain_k": 11, "mod": 12,
     "gain_cq": 13, "gain_ck": 14, "w_qkv": 15, "b_qkv": 16, "w_o": 17, "b_o": 18,
     "w_cq": 19, "b_cq": 20, "w_ckv": 21, "b_ckv": 22, "w_co": 23, "b_co": 24, "context": 25,
+    "img_context": 26, "w_ikv": 27, "b_ikv": 28, "gain_ik": 29, "ffn_out": 30,
     "rows": 99,
 }
+
+
+IMAGE_TOKENS = 257
 
 
 def seed_of(workload_index: int, tag: str, salt: int = 0) -> int:
@@ -50,20 +57,22 @@ def tensor(w, tag: str, device, salt: int = 0) -> torch.Tensor:
     """One named input of workload ``w`` (a ``workloads.Workload``)."""
     B, L, C, Lt = w.batch, w.tokens, w.dim, w.text_len
     s = seed_of(w.index, tag, salt)
-    if tag in ("x", "y", "q", "k", "v", "cross_q", "cross_y"):
+    if tag in ("x", "y", "q", "k", "v", "cross_q", "cross_y", "ffn_out"):
         return normal((B, L, C), s, device)
     if tag in ("text_k", "text_v"):
         return normal((B, Lt, C), s, device)
-    if tag in ("gain_q", "gain_k", "gain_cq", "gain_ck"):
+    if tag in ("gain_q", "gain_k", "gain_cq", "gain_ck", "gain_ik"):
         return normal((C,), s, device, std=0.1, mean=1.0, dtype=torch.float32)
-    if tag in ("w_qkv", "w_o", "w_cq", "w_ckv", "w_co"):
-        rows = {"w_qkv": 3 * C, "w_ckv": 2 * C}.get(tag, C)
+    if tag in ("w_qkv", "w_o", "w_cq", "w_ckv", "w_co", "w_ikv"):
+        rows = {"w_qkv": 3 * C, "w_ckv": 2 * C, "w_ikv": 2 * C}.get(tag, C)
         return normal((rows, C), s, device, std=C ** -0.5)
-    if tag in ("b_qkv", "b_o", "b_cq", "b_ckv", "b_co"):
-        n = {"b_qkv": 3 * C, "b_ckv": 2 * C}.get(tag, C)
+    if tag in ("b_qkv", "b_o", "b_cq", "b_ckv", "b_co", "b_ikv"):
+        n = {"b_qkv": 3 * C, "b_ckv": 2 * C, "b_ikv": 2 * C}.get(tag, C)
         return normal((n,), s, device, std=C ** -0.5, dtype=torch.float32)
     if tag == "context":
         return normal((B, Lt, C), s, device)
+    if tag == "img_context":
+        return normal((B, IMAGE_TOKENS, C), s, device)
     if tag == "mod":
         return normal((B, 6, C), s, device, std=0.1 ** 0.5, dtype=torch.float32)
     raise KeyError(tag)

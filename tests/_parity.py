@@ -50,3 +50,42 @@ def compare(name: str, got_bits: np.ndarray, ref64: np.ndarray, max_abs: float =
     assert stats["mean_abs"] <= mean_abs, f"{name}: mean-abs {stats['mean_abs']}"
     assert over.sum() <= max(1, MAX_FLIP_FRACTION * d.size), f"{name}: too many flips {stats}"
     return stats
+
+
+
+def compare_chain(name: str, got_bits: np.ndarray, ref64: np.ndarray) -> dict:
+    """Comparison after several dependent library calls.
+
+    Both chains round to bf16 at every library output, so each upstream
+    call's error (a rounding-boundary flip of one quantum, or the up to 1e-3
+    mean error one call is allowed) is carried into every later value and
+    moves later values across their own rounding boundaries; the difference
+    grows along the chain (measured: mean-abs 1e-4 after the first residual,
+    9e-4 six calls later). The bound for a chain takes the per-call budget
+    twice (quadrature growth over about four dependent calls): mean-abs
+    2e-3, elements beyond 1e-2 at most 2%, each element within four quanta
+    of the reference or 2e-2, and the relative L2 error within 4e-3 (two
+    bf16 unit roundoffs). A systematic error in any call (a dropped term,
+    wrong gate or bias, wrong row) moves the relative L2 error by far more.
+    """
+    got = O.bf16_bits_to_f64(got_bits)
+    ref = O.bf16_round(ref64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    d = np.abs(got - ref)
+    allowed = np.maximum(2 * MAX_ABS, 4 * bf16_quantum(ref))
+    over = d > MAX_ABS
+    stats = {
+        "n": int(d.size),
+        "max_abs": float(d.max()) if d.size else 0.0,
+        "mean_abs": float(d.mean()) if d.size else 0.0,
+        "over_1e-2": int(over.sum()),
+        "rel_l2": float(np.linalg.norm(got - ref64) / max(np.linalg.norm(ref64), 1e-300)),
+    }
+    print(f"[parity chain] {name}: {stats}", flush=True)
+    bad = d > allowed
+    assert not bad.any(), f"{name}: {int(bad.sum())} elements beyond four quanta: {stats}"
+    assert stats["mean_abs"] <= 2 * MEAN_ABS, f"{name}: mean-abs {stats['mean_abs']}"
+    assert over.sum() <= max(1, 2e-2 * d.size), f"{name}: too many elements over 1e-2 {stats}"
+    assert stats["rel_l2"] <= 4e-3, f"{name}: relative L2 error {stats['rel_l2']}"
+    return stats
