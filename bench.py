@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the oracle sample on the host")
+    p.add_argument("--with-projections", action="store_true",
+                   help="also time the block with its q/k/v/o and cross projections "
+                        "(wan_linear_fwd) included (stderr only)")
     p.add_argument("--chunk-frames", type=int, default=0,
                    help="also time chunk-causal self-attention with chunks of this many "
                         "latent frames (stderr only)")
@@ -107,6 +110,51 @@ def cpu_baseline(w, tensors, budget_s: float):
         "sample": f"self-attention of {len(rows)} query rows x {pairs} (batch, head) pairs of "
                   f"{w.name} (L={w.tokens}), float64 NumPy, {dt:.1f} s incl. host copies",
     }
+
+
+def breakdown_projections(args, w, ops, synth, t, per):
+    """Time the projections of one block (fused q/k/v, o, cross q, fused
+    cross k/v over the text context, cross o) with wan_linear_fwd and report
+    the block time with them included."""
+    import torch
+    dev = t["x"].device
+    B, L, C, Lt = w.batch, w.tokens, w.dim, w.text_len
+    wt = {n: synth.tensor(w, n, dev) for n in
+          ("w_qkv", "b_qkv", "w_o", "b_o", "w_cq", "b_cq", "w_ckv", "b_ckv", "w_co", "b_co",
+           "context")}
+    emp = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+    qkv, y, cq, ckv, yc = emp(B, L, 3 * C), emp(B, L, C), emp(B, L, C), emp(B, Lt, 2 * C), \
+        emp(B, L, C)
+    calls = [("qkv", t["x"], "w_qkv", "b_qkv", qkv, B * L, 3 * C),
+             ("o", t["y"], "w_o", "b_o", y, B * L, C),
+             ("cross_q", t["x"], "w_cq", "b_cq", cq, B * L, C),
+             ("cross_kv", wt["context"], "w_ckv", "b_ckv", ckv, B * Lt, 2 * C),
+             ("cross_o", t["y"], "w_co", "b_co", yc, B * L, C)]
+    for _ in range(args.warmup):
+        for _, xin, wn, bn, out, _, _ in calls:
+            ops.linear_fwd(xin, wt[wn], wt[bn], out=out)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
+    for s in range(args.steps):
+        for i, (_, xin, wn, bn, out, _, _) in enumerate(calls):
+            ev[s][i].record()
+            ops.linear_fwd(xin, wt[wn], wt[bn], out=out)
+        ev[s][-1].record()
+    torch.cuda.synchronize()
+    rec, total_ms, total_flop = {}, 0.0, 0.0
+    for i, (name, _, _, _, _, M, N) in enumerate(calls):
+        ms = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+        flop = 2.0 * M * N * C
+        total_ms += ms
+        total_flop += flop
+        tf = flop / (ms * 1e-3) / 1e12
+        rec[name] = {"ms": round(ms, 3), "tflops": round(tf, 1),
+                     "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    block_ms = sum(per.values()) + total_ms
+    print(json.dumps({"projections": rec, "projections_ms": round(total_ms, 3),
+                      "projections_tflop": round(total_flop / 1e12, 2),
+                      "block_ms_with_projections": round(block_ms, 3)}), file=sys.stderr,
+          flush=True)
 
 
 def breakdown_causal(args, w, ops, q, k, v, o, full_ms):
@@ -236,6 +284,9 @@ def main():
             rec.update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
         breakdown[n] = rec
     print(json.dumps({"breakdown": breakdown}), file=sys.stderr, flush=True)
+
+    if args.with_projections:
+        breakdown_projections(args, w, ops, synth, t, per)
 
     if args.chunk_frames > 0:
         breakdown_causal(args, w, ops, qr, kr, t["v"], o, per["self_attn"])
