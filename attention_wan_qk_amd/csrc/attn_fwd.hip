@@ -26,12 +26,14 @@
 //  * The running max is in log2 units of the scaled scores; it is only moved
 //    (and O, l rescaled) when some row's tile max exceeds it by more than 8,
 //    so the exponentials stay <= 2^8 and the rescale is rare.
-//  * K/V tiles are double-buffered in LDS; the buffer loads of the next tiles
-//    are in flight during two phases before they are stored to LDS. Rows past
-//    k_len fall outside the buffer resource and read as zero. Each 16-byte
-//    chunk of a row is XOR-swizzled so the MFMA operand reads are
-//    bank-conflict free; the loads pick, for lane i, the global chunk that
-//    belongs at base + 16 i, so the stores stay lane-linear.
+//  * K/V tiles are double-buffered in LDS and loaded by the waves of group 0
+//    with buffer loads whose destination is the LDS (no register staging):
+//    issued right after their GEMM phase (once its LDS reads are done), they
+//    complete during the following softmax phase, which reads no LDS. Rows
+//    past k_len fall outside the buffer resource and read as zero. Each
+//    16-byte chunk of a row is XOR-swizzled so the MFMA operand reads are
+//    bank-conflict free; a load writes 16 bytes per lane at base + 16 lane,
+//    so each lane fetches the global chunk that belongs there.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
 #include "wan_device.h"
@@ -55,11 +57,12 @@ constexpr int kHD = 128;                     // head size
 constexpr int kRowBytes = kHD * 2;
 constexpr int kTileBytes = kBN * kRowBytes;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB per load instruction
+constexpr int kLoadsPerWave = kTileBytes / 1024 / (kWaves / 2);  // group-0 waves, 1 KiB each
 constexpr float kRescaleThreshold = 8.0f;    // log2 units
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
@@ -68,6 +71,21 @@ template <int N>
 struct Int {
   static constexpr int value = N;
 };
+
+// s_waitcnt vmcnt(0): wait for this wave's outstanding buffer loads only.
+constexpr int kWaitLoads = 0x0F70;
+
+// Barrier between phases, without a memory fence. The only LDS writes inside
+// the main loop are the group-0 buffer loads into LDS; their waves wait for
+// them (kWaitLoads) before the barrier that publishes them. Every LDS read of
+// a phase feeds an MFMA issued before that phase's barrier, so it has
+// completed. The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -134,40 +152,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
 
-  // Per-lane global offsets of this wave's tile loads: load i of wave w
-  // fills tile rows 4(kLoadsPerWave w + i) .. +3; lane l stores physical
-  // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, which holds logical
-  // chunk (l % 16) ^ swizzle.
+  // The waves of group 0 move the K and V tiles from global memory straight
+  // into LDS (buffer loads with the LDS as destination). Load i of wave w
+  // fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
+  // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so it fetches the
+  // logical chunk (l % 16) ^ swizzle of that row.
   uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int r = (wave * kLoadsPerWave + i) * 4 + (lane >> 4);
+    const int r = ((wave & 3) * kLoadsPerWave + i) * 4 + (lane >> 4);
     const int p = lane & 15;
     vo_k[i] = r * row_k + (k_phys(r, p) << 4);  // k_phys is an involution
     vo_v[i] = r * row_v + (v_phys(r, p) << 4);
   }
-  u32x4 kreg[kLoadsPerWave], vreg[kLoadsPerWave];
-  auto load_k = [&](int t) {
+  auto dma_k = [&](int t, int slot) {
     const uint32_t sk = (uint32_t)t * kBN * row_k;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo_k[i], sk, 0);
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (lds_void*)(Ks + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
+          vo_k[i], sk, 0, 0);
   };
-  auto load_v = [&](int t) {
+  auto dma_v = [&](int t, int slot) {
     const uint32_t sv = (uint32_t)t * kBN * row_v;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_v[i], sv, 0);
-  };
-  auto store_k = [&](int slot) {
-#pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
-      *reinterpret_cast<u32x4*>(Ks + slot * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16) = kreg[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (lds_void*)(Vs + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
+          vo_v[i], sv, 0, 0);
   };
-  auto store_v = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i)
-      *reinterpret_cast<u32x4*>(Vs + slot * kTileBytes + (wave * kLoadsPerWave + i) * 1024 + lane * 16) = vreg[i];
-  };
-
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
   const int qrow = qt * kBM + wave * 32 + r32;
   const int lim_row = key_limit(min(qrow, a.Lq - 1));
@@ -178,10 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
   }
 
-  if (nT > 0) {
-    load_k(0);
-    store_k(0);
-  }
+  if (nT > 0 && group == 0) dma_k(0, 0);
   __builtin_amdgcn_s_waitcnt(0);   // Q and K tile 0 have landed
   __syncthreads();
 
@@ -324,45 +334,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   // behind group 0, so that in every interval one wave of each SIMD is in a
   // GEMM phase (MFMA) while the other is in a softmax phase (VALU):
   //   phase 2j: GEMM(j) = PV(j-1) + S(j);   phase 2j+1: softmax(j).
-  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
-  // loads of K(j+1) and V(j) start at interval 2j and are stored at the end
-  // of interval 2j+1 into the slots freed by K(j-1) and V(j-2).
+  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1.
+  // Group 0 loads K(j+1) and V(j) into the slots freed by K(j-1) and V(j-2)
+  // right after its GEMM phase of interval 2j and waits for them at the end
+  // of interval 2j+1, before the barrier that publishes them.
   const int nIntervals = 2 * nT + 2;
   for (int i = 0; i < nIntervals; i += 4) {
-    const int j0 = i >> 1;            // even tile index of this round
-    // interval i (tile j0)
-    if (j0 < nT) {
-      if (j0 + 1 < nT) load_k(j0 + 1);
-      load_v(j0);
-    }
-    if (group == 0) gemm(Int<0>{}, j0);
-    else softmax(j0 - 1);
-    __syncthreads();
-    // interval i + 1
-    if (group == 0) softmax(j0);
-    else gemm(Int<0>{}, j0);
-    if (j0 < nT) {
-      if (j0 + 1 < nT) store_k(1);
-      store_v(0);
-    }
-    __syncthreads();
-    // interval i + 2 (tile j0 + 1)
+    const int j0 = i >> 1;
+    if (group == 0) {
+      gemm(Int<0>{}, j0);
+      if (j0 < nT) {
+        if (j0 + 1 < nT) dma_k(j0 + 1, 1);
+        dma_v(j0, 0);
+      }
+    } else softmax(j0 - 1);
+    phase_barrier();
+    if (group == 0) {
+      softmax(j0);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);   // this wave's tile loads landed
+    } else gemm(Int<0>{}, j0);
+    phase_barrier();
     const int j1 = j0 + 1;
-    if (j1 < nT) {
-      if (j1 + 1 < nT) load_k(j1 + 1);
-      load_v(j1);
-    }
-    if (group == 0) gemm(Int<1>{}, j1);
-    else softmax(j0);
-    __syncthreads();
-    // interval i + 3
-    if (group == 0) softmax(j1);
-    else gemm(Int<1>{}, j1);
-    if (j1 < nT) {
-      if (j1 + 1 < nT) store_k(0);
-      store_v(1);
-    }
-    __syncthreads();
+    if (group == 0) {
+      gemm(Int<1>{}, j1);
+      if (j1 < nT) {
+        if (j1 + 1 < nT) dma_k(j1 + 1, 0);
+        dma_v(j1, 1);
+      }
+    } else softmax(j0);
+    phase_barrier();
+    if (group == 0) {
+      softmax(j1);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);   // this wave's tile loads landed
+    } else gemm(Int<1>{}, j1);
+    phase_barrier();
   }
 
   // ---- epilogue: combine the two half-waves' partial sums, normalise, store.
