@@ -29,4 +29,9 @@ from .wan_oracle import (  # noqa: F401
     chunk_causal_visible,
     chunk_causal_attention,
     linear,
+    e4m3_bits_to_f64,
+    f64_to_e4m3_bits,
+    quantize_int8_blocks,
+    quantize_v_mxfp8,
+    attention_8bit,
 )

@@ -393,3 +393,164 @@ def linear(x, w, bias=None) -> np.ndarray:
     if bias is not None:
         y = y + _f64(bias)
     return y
+
+
+# ----------------------------------------------------------------------------
+# 8-bit attention (the pages' inference speed path)
+# ----------------------------------------------------------------------------
+# "论文专题讲解：Wan2.1", inference-optimisation table, row "8-bit
+# FlashAttention": S = Q K^T in INT8, O = P V in FP8, accumulation across
+# key blocks in FP32. Readings (the table gives no more): Q and K are
+# quantised per (batch, head, block of 64 tokens) to symmetric INT8 with an
+# fp32 scale amax / 127; V is quantised to FP8 E4M3 per (batch, head,
+# channel, block of 32 keys) with a power-of-two (E8M0) scale, the OCP
+# microscaling recipe; P is rounded to FP8 E4M3 after the row maximum (an
+# integer in log2 units) is subtracted, and the softmax denominator sums the
+# unrounded P. Every quantised code is decided in fp32, as the kernel decides
+# it (numpy float32 arithmetic is IEEE-correctly rounded, like the GPU's).
+INT8_BLOCK = 64
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+LOG2E = 1.4426950408889634
+
+
+def e4m3_bits_to_f64(bits) -> np.ndarray:
+    """Decode OCP FP8 E4M3FN codes (bias 7, no infinities, S.1111.111 = NaN)."""
+    b = np.asarray(bits).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return s * mag
+
+
+def f64_to_e4m3_bits(x) -> np.ndarray:
+    """Round to the nearest E4M3FN value, ties to even mantissa; magnitudes
+    past 464 (halfway from 448 to the NaN code; 464 itself ties to 448) and
+    NaN give the NaN code (no saturation, as the format conversion does)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.clip(ex - 1, -6, 8)                  # exponent of the binade (subnormals use -6)
+    q = np.ldexp(1.0, e - 3)                    # spacing of representable values there
+    n = np.rint(a / q)                          # ties to even
+    val = n * q
+    e2 = np.clip(np.frexp(np.where(val > 0, val, 1.0))[1] - 1, -6, 8)
+    normal = val >= 2.0 ** -6
+    mant = np.where(normal, np.rint(val / np.ldexp(1.0, e2 - 3)) - 8, np.rint(val / 2.0 ** -9))
+    code = np.where(normal, ((e2 + 7) << 3) + mant.astype(np.int64), mant.astype(np.int64))
+    code = np.where((a > 464.0) | np.isnan(x), 0x7F, code)
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_int8_blocks(x, H: int, block: int = INT8_BLOCK):
+    """Symmetric INT8 per (batch, head, block of ``block`` tokens).
+
+    x: [B, L, H*d]. Returns codes int8 [B, H, L, d] and scales float32
+    [B, H, ceil(L / block)]: amax = max |x| over the block (all L tokens, key
+    lengths play no part), code = round_half_even(x * (127 / amax)) in fp32,
+    clamped to +-127, scale = amax / 127 in fp32 (amax = 0: codes 0, scale 0).
+    """
+    x = _f64(x)
+    B, L, C = x.shape
+    d = C // H
+    nb = -(-L // block)
+    xh = x.reshape(B, L, H, d).transpose(0, 2, 1, 3).astype(np.float32)   # exact (bf16 -> f32)
+    codes = np.zeros((B, H, L, d), dtype=np.int8)
+    scales = np.zeros((B, H, nb), dtype=np.float32)
+    for j in range(nb):
+        blk = xh[:, :, j * block:(j + 1) * block]
+        amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
+        safe = np.where(amax > 0, amax, np.float32(1))
+        inv = (np.float32(127) / safe).astype(np.float32)
+        c = np.rint((blk * inv[:, :, None, None]).astype(np.float32))
+        c = np.where(amax[:, :, None, None] > 0, np.clip(c, -127, 127), 0)
+        codes[:, :, j * block:(j + 1) * block] = c.astype(np.int8)
+        scales[:, :, j] = np.where(amax > 0, (amax / np.float32(127)).astype(np.float32), 0)
+    return codes, scales
+
+
+def quantize_v_mxfp8(v, H: int, block: int = MX_BLOCK):
+    """FP8 E4M3 per (batch, head, channel, block of ``block`` keys) with a
+    power-of-two scale (OCP microscaling): X = 2^(floor(log2 amax) - 8), the
+    largest E4M3 binade being 2^8; element = E4M3(clamp(v / X, +-448)).
+
+    v: [B, L, H*d]. Returns codes uint8 [B, H, L, d], the scale exponents
+    int [B, H, ceil(L / block), d] (X = 2^exp; amax = 0 gives exp -127 and
+    zero codes) and the dequantised values float64 [B, H, L, d].
+    """
+    v = _f64(v)
+    B, L, C = v.shape
+    d = C // H
+    nb = -(-L // block)
+    vh = v.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    codes = np.zeros((B, H, L, d), dtype=np.uint8)
+    exps = np.full((B, H, nb, d), -127, dtype=np.int64)
+    deq = np.zeros((B, H, L, d))
+    for j in range(nb):
+        blk = vh[:, :, j * block:(j + 1) * block]
+        amax = np.abs(blk).max(axis=2)                               # [B, H, d]
+        _, fe = np.frexp(np.where(amax > 0, amax, 1.0))
+        ex = np.where(amax > 0, (fe - 1) - 8, -127)
+        scaled = np.clip(blk / np.ldexp(1.0, ex)[:, :, None, :], -E4M3_MAX, E4M3_MAX)
+        c = f64_to_e4m3_bits(scaled)
+        codes[:, :, j * block:(j + 1) * block] = c
+        exps[:, :, j] = ex
+        deq[:, :, j * block:(j + 1) * block] = (e4m3_bits_to_f64(c)
+                                                * np.ldexp(1.0, ex)[:, :, None, :])
+    return codes, exps, deq
+
+
+def _f32_fma(a, b, c) -> np.ndarray:
+    """fp32 fused multiply-add: the product of two fp32 values is exact in
+    float64, the sum is rounded once more to fp32."""
+    return (np.asarray(a, np.float64) * np.asarray(b, np.float64)
+            + np.asarray(c, np.float64)).astype(np.float32)
+
+
+def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
+    """8-bit self-attention: INT8 scores, FP8 probabilities and values, fp32
+    accumulation (see the section comment for the readings).
+
+    q, k, v: [B, L, H*d]. Per (b, h) and query row i, with n = k_len:
+      S_ij   = sum_d qc_id kc_jd                    (exact integer dot product)
+      mult   = fp32(fp32(sq_blk(i) sk_blk(j)) c),   c = fp32(scale log2 e)
+      m_i    = ceil(max_j S_ij mult) - 7            (integer, log2 units)
+      t_ij   = fp32 fma(S_ij, mult, -m_i);  p_ij = fp32(2^t_ij);  P_ij = E4M3(p_ij)
+      o_i    = sum_j P_ij vdeq_j / sum_j p_ij,   lse_i = ln 2 (m_i + log2 sum_j p_ij)
+    Returns o [B, rows, H*d] and lse [B, H, rows]; n = 0 gives o = 0,
+    lse = -inf. The integer offset m_i only moves P by a power of two, which
+    leaves every normal E4M3 rounding unchanged.
+    """
+    qc, sq = quantize_int8_blocks(q, H)
+    kc, sk = quantize_int8_blocks(k, H)
+    _, _, vdeq = quantize_v_mxfp8(v, H)
+    B, _, Lq, d = qc.shape
+    Lk = kc.shape[2]
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    c = np.float32(scale * LOG2E)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, rows.size, H * d))
+    lse = np.full((B, H, rows.size), -np.inf)
+    kblk = np.arange(Lk) // INT8_BLOCK
+    qblk = rows // INT8_BLOCK
+    for b in range(B):
+        n = Lk if k_lens is None else max(0, min(int(k_lens[b]), Lk))
+        if n == 0:
+            continue
+        for h in range(H):
+            S = qc[b, h, rows].astype(np.int64) @ kc[b, h, :n].astype(np.int64).T
+            sqk = (sq[b, h, qblk][:, None] * sk[b, h, kblk[:n]][None, :]).astype(np.float32)
+            mult = (sqk * c).astype(np.float32)
+            m = np.ceil((S * mult.astype(np.float64)).max(axis=1)) - 7
+            t = _f32_fma(S.astype(np.float32), mult, -m[:, None])
+            p = np.exp2(t.astype(np.float64)).astype(np.float32).astype(np.float64)
+            P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))
+            l = p.sum(axis=1)
+            o[b, :, h * d:(h + 1) * d] = (P @ vdeq[b, h, :n]) / l[:, None]
+            lse[b, h] = np.log(2.0) * (m + np.log2(l))
+    return o, lse

@@ -497,3 +497,152 @@ def test_linear_special_cases_and_torch():
     xb = np.array([[0x3F80, 0x4000]], dtype=np.uint16)
     wb = np.array([[0x4000, 0x3F80]], dtype=np.uint16)
     assert O.linear(xb, wb)[0, 0] == 4.0
+
+
+# ---------------------------------------------------------------- 8-bit ----
+def test_e4m3_codec_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = O.e4m3_bits_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(mine)], ref[~np.isnan(ref)])
+    finite = mine[~np.isnan(mine)]
+    assert finite.max() == 448.0 and np.min(finite[finite > 0]) == 2.0 ** -9
+    # random magnitudes over every binade, exact ties between neighbours, out of range
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(100000) * np.exp2(rng.uniform(-12, 9.5, 100000))
+    pos = np.sort(finite[finite > 0])
+    ties = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([x, ties, -ties, [464.0, 470.0, -1e4, 0.0, 2.0 ** -11]]).astype(np.float32)
+    got = O.f64_to_e4m3_bits(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_int8_block_quantization():
+    B, L, H, d = 2, 150, 2, 16          # blocks of 64, 64, 22 tokens
+    x = RNG.standard_normal((B, L, H * d)) * 3
+    x[1, 64:128, :d] = 0.0              # one all-zero block
+    codes, sc = O.quantize_int8_blocks(x, H)
+    assert codes.shape == (B, H, L, d) and sc.shape == (B, H, 3)
+    xh = x.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    for b in range(B):
+        for h in range(H):
+            for j in range(3):
+                blk = xh[b, h, j * 64:(j + 1) * 64]
+                c = codes[b, h, j * 64:(j + 1) * 64].astype(np.float64)
+                amax = np.abs(blk).max()
+                if amax == 0:
+                    assert sc[b, h, j] == 0 and not c.any()
+                    continue
+                assert sc[b, h, j] == np.float32(np.float32(amax) / np.float32(127))
+                assert np.abs(c).max() == 127                       # the block max maps to +-127
+                assert np.all(np.abs(c * sc[b, h, j] - blk) <= sc[b, h, j] * 0.5001)
+    # one element by hand: code = round_half_even(fp32(x * fp32(127 / amax)))
+    b, h, i, e = 0, 1, 70, 5
+    amax = np.float32(np.abs(xh[b, h, 64:128]).max())
+    inv = np.float32(np.float32(127) / amax)
+    assert codes[b, h, i, e] == np.rint(np.float32(np.float32(xh[b, h, i, e]) * inv))
+
+
+def test_mxfp8_value_quantization():
+    B, L, H, d = 1, 80, 1, 8            # key blocks of 32, 32, 16
+    v = RNG.standard_normal((B, L, H * d)) * np.exp2(RNG.integers(-6, 6, size=(1, 1, H * d)))
+    v[0, 32:64, 3] = 0.0                 # a zero block
+    codes, ex, deq = O.quantize_v_mxfp8(v, H)
+    for j in range(3):
+        for c in range(d):
+            blk = v[0, j * 32:(j + 1) * 32, c]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert ex[0, 0, j, c] == -127 and not codes[0, 0, j * 32:(j + 1) * 32, c].any()
+                continue
+            e = math.frexp(amax)[1] - 1 - 8                      # floor(log2 amax) - 8
+            assert ex[0, 0, j, c] == e
+            scaled = blk / 2.0 ** e
+            assert 256 <= np.abs(scaled).max() < 512
+            r = deq[0, 0, j * 32:(j + 1) * 32, c]
+            small = np.abs(scaled) < 2.0 ** -6
+            big = np.abs(scaled) >= E4M3_CLAMP
+            rel = np.abs(r - blk) / np.abs(np.where(blk == 0, 1, blk))
+            assert np.all(rel[~small & ~big] <= 2.0 ** -4 + 1e-12)   # half a quantum of 2^-3
+            assert np.all(np.abs(r[big]) == 448 * 2.0 ** e)          # clamped to the largest code
+
+
+E4M3_CLAMP = 448.0
+
+
+def _attention_8bit_loops(q, k, v, H, k_len, scale):
+    """The 8-bit algorithm written with scalar loops (tiny inputs only)."""
+    qc, sq = O.quantize_int8_blocks(q, H)
+    kc, sk = O.quantize_int8_blocks(k, H)
+    _, _, vd = O.quantize_v_mxfp8(v, H)
+    B, _, L, d = qc.shape
+    c = np.float32(scale * 1.4426950408889634)
+    out = np.zeros((B, L, H * d))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                ts, mults = [], []
+                for j in range(k_len):
+                    s = sum(int(qc[b, h, i, e]) * int(kc[b, h, j, e]) for e in range(d))
+                    mult = np.float32(np.float32(sq[b, h, i // 64] * sk[b, h, j // 64]) * c)
+                    ts.append(s)
+                    mults.append(mult)
+                m = math.ceil(max(s * float(mu) for s, mu in zip(ts, mults))) - 7
+                num = np.zeros(d)
+                den = 0.0
+                for j, (s, mu) in enumerate(zip(ts, mults)):
+                    t = np.float32(float(np.float32(s)) * float(mu) - m)
+                    p = float(np.float32(2.0 ** float(t)))
+                    P = float(O.e4m3_bits_to_f64(O.f64_to_e4m3_bits(p)))
+                    num += P * vd[b, h, j]
+                    den += p
+                out[b, i, h * d:(h + 1) * d] = num / den
+    return out
+
+
+def test_attention_8bit_against_loops():
+    B, L, H, d = 1, 70, 2, 16
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    o, lse = O.attention_8bit(q, k, v, H, k_lens=[61], scale=0.3)
+    ref = _attention_8bit_loops(q, k, v, H, 61, 0.3)
+    assert np.allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_8bit_properties():
+    B, L, H, d = 2, 150, 2, 32
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    o, lse = O.attention_8bit(q, k, v, H)
+    # close to exact attention on the unquantised inputs
+    ex, exl = O.self_attention(q, k, v, H)
+    assert np.sqrt(np.mean((o - ex) ** 2)) < 0.06 * np.sqrt(np.mean(ex ** 2))
+    # against exact attention on the dequantised operands, only P's rounding differs:
+    # |o - o'| <= 2^-4 max|v| + (keys) 2^-10 max|v| / sum p
+    qc, sq = O.quantize_int8_blocks(q, H)
+    kc, sk = O.quantize_int8_blocks(k, H)
+    _, _, vd = O.quantize_v_mxfp8(v, H)
+    blk = np.arange(L) // 64
+    for b in range(B):
+        for h in range(H):
+            S = (qc[b, h].astype(np.float64) * sq[b, h, blk][:, None]) @ \
+                (kc[b, h].astype(np.float64) * sk[b, h, blk][:, None]).T / np.sqrt(d)
+            w = np.exp(S - S.max(axis=1, keepdims=True))
+            od = (w @ vd[b, h]) / w.sum(axis=1, keepdims=True)
+            vmax = np.abs(vd[b, h]).max()
+            assert np.all(np.abs(o[b, :, h * d:(h + 1) * d] - od) <= (2 ** -4 + L * 2 ** -10) * vmax)
+    # all logits equal (q = 0): p = 2^7 exactly for every key, so o is the mean of the
+    # dequantised values
+    oz, lz = O.attention_8bit(np.zeros_like(q), k, v, H)
+    for h in range(H):
+        assert np.allclose(oz[:, :, h * d:(h + 1) * d], vd[:, h].mean(axis=1, keepdims=True),
+                           rtol=0, atol=1e-12)
+    assert np.allclose(lz, np.log(L))
+    # key lengths: k_len 0 gives zeros and -inf; keys in blocks wholly past k_len do nothing
+    o0, l0 = O.attention_8bit(q, k, v, H, k_lens=[0, 128])
+    assert not o0[0].any() and np.all(np.isneginf(l0[0]))
+    k2, v2 = k.copy(), v.copy()
+    k2[1, 128:] = 9.0
+    v2[1, 128:] = -7.0
+    o1, _ = O.attention_8bit(q, k2, v2, H, k_lens=[0, 128])
+    assert np.array_equal(o0[1], o1[1])
