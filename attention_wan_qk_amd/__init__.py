@@ -19,7 +19,9 @@ from .ops import (  # noqa: F401
     cross_attn_fwd,
     linear_fwd,
     qk_norm_rope3d,
+    quantize_qkv_8bit,
     self_attn_fwd,
+    self_attn_fwd_8bit,
 )
 
 __version__ = "0.1.0"

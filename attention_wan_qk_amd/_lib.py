@@ -38,6 +38,10 @@ SIGNATURES = {
     "wan_adaln_modulate_gate": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _F,
                                      _P]),
     "wan_linear_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _P]),
+    "wan_quantize_qkv_8bit": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L,
+                                   _L, _P]),
+    "wan_self_attn_fwd_8bit": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L,
+                                    _F, _P]),
 }
 
 _lib = None

@@ -359,4 +359,98 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w, const float* b
   return from_hip(wan::launch_linear(a, stream));
 }
 
+wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8, float* q_scale,
+                                  float* k_scale, uint8_t* v_scale, const void* q, const void* k,
+                                  const void* v, int B, int L, int H, int D, int64_t ld_q,
+                                  int64_t ld_k, int64_t ld_v, hipStream_t stream) {
+  if (B < 0 || L < 0 || H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+  if (D != kHeadDim) return WAN_ERROR_NOT_SUPPORTED;
+  if ((int64_t)B * L == 0) return WAN_SUCCESS;
+  const void* ptrs[9] = {q8, k8, v8, q_scale, k_scale, v_scale, q, k, v};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t C = (int64_t)H * D;
+  if (C > (int64_t)1 << 24) return WAN_ERROR_NOT_SUPPORTED;
+  int64_t* lds[3] = {&ld_q, &ld_k, &ld_v};
+  for (int64_t* ld : lds) {
+    if (*ld == 0) *ld = C;
+    if (*ld < C || (*ld & 7)) return WAN_ERROR_INVALID_VALUE;
+  }
+  // outputs: codes B*H*nT*64*D bytes each, scales B*H*nT floats / B*H*nT*256 bytes
+  const int64_t nT = (L + 63) / 64, tiles = (int64_t)B * H * nT;
+  const Range outs[6] = {
+      {reinterpret_cast<uintptr_t>(q8), reinterpret_cast<uintptr_t>(q8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(k8), reinterpret_cast<uintptr_t>(k8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(v8), reinterpret_cast<uintptr_t>(v8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(q_scale), reinterpret_cast<uintptr_t>(q_scale) + (uintptr_t)(tiles * 4)},
+      {reinterpret_cast<uintptr_t>(k_scale), reinterpret_cast<uintptr_t>(k_scale) + (uintptr_t)(tiles * 4)},
+      {reinterpret_cast<uintptr_t>(v_scale), reinterpret_cast<uintptr_t>(v_scale) + (uintptr_t)(tiles * 256)}};
+  const int64_t rows = (int64_t)B * L;
+  const Range ins[3] = {span_bf16(q, rows, ld_q, C), span_bf16(k, rows, ld_k, C),
+                        span_bf16(v, rows, ld_v, C)};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return WAN_ERROR_INVALID_VALUE;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return WAN_ERROR_INVALID_VALUE;
+  }
+  wan::Quant8Args a{q8, k8, v8, q_scale, k_scale, v_scale, q, k, v, B, L, H, ld_q, ld_k, ld_v};
+  return from_hip(wan::launch_quant8(a, stream));
+}
+
+wanStatus_t wan_self_attn_fwd_8bit(void* o, float* lse, const int8_t* q8, const int8_t* k8,
+                                   const uint8_t* v8, const float* q_scale,
+                                   const float* k_scale, const uint8_t* v_scale,
+                                   const int32_t* k_lens, int B, int L, int H, int D,
+                                   int64_t ld_o, float softmax_scale, hipStream_t stream) {
+  if (B < 0 || L < 0 || H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+  if (D != kHeadDim) return WAN_ERROR_NOT_SUPPORTED;
+  if ((int64_t)B * L == 0) return WAN_SUCCESS;
+  const void* ptrs[7] = {o, q8, k8, v8, q_scale, k_scale, v_scale};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return WAN_ERROR_INVALID_VALUE;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t C = (int64_t)H * D;
+  if (C > (int64_t)1 << 24) return WAN_ERROR_NOT_SUPPORTED;
+  if (ld_o == 0) ld_o = C;
+  if (ld_o < C || (ld_o & 7)) return WAN_ERROR_INVALID_VALUE;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return WAN_ERROR_INVALID_VALUE;
+  const int64_t nT = (L + 63) / 64, tiles = (int64_t)B * H * nT;
+  if (nT > 4096) return WAN_ERROR_NOT_SUPPORTED;   // key-block scales held in LDS
+  const Range ro = span_bf16(o, (int64_t)B * L, ld_o, C);
+  const Range ins[6] = {
+      {reinterpret_cast<uintptr_t>(q8), reinterpret_cast<uintptr_t>(q8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(k8), reinterpret_cast<uintptr_t>(k8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(v8), reinterpret_cast<uintptr_t>(v8) + (uintptr_t)(tiles * 64 * D)},
+      {reinterpret_cast<uintptr_t>(q_scale), reinterpret_cast<uintptr_t>(q_scale) + (uintptr_t)(tiles * 4)},
+      {reinterpret_cast<uintptr_t>(k_scale), reinterpret_cast<uintptr_t>(k_scale) + (uintptr_t)(tiles * 4)},
+      {reinterpret_cast<uintptr_t>(v_scale), reinterpret_cast<uintptr_t>(v_scale) + (uintptr_t)(tiles * 256)}};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return WAN_ERROR_INVALID_VALUE;
+  if (lse) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(lse);
+    const Range rl{lo, lo + (uintptr_t)((int64_t)B * H * L * 4)};
+    if (overlap(rl, ro)) return WAN_ERROR_INVALID_VALUE;
+    for (const Range& r : ins)
+      if (overlap(rl, r)) return WAN_ERROR_INVALID_VALUE;
+  }
+  wan::Attn8Args a{};
+  a.o = o;
+  a.lse = lse;
+  a.q8 = q8;
+  a.k8 = k8;
+  a.v8 = v8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_lens = k_lens;
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.ld_o = ld_o;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return from_hip(wan::launch_attn8_fwd(a, stream));
+}
+
 }  // extern "C"

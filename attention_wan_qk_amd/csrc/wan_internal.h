@@ -59,10 +59,41 @@ struct LinearArgs {
   int64_t ld_x, ld_w, ld_y;
 };
 
+struct Quant8Args {
+  int8_t* q8;
+  int8_t* k8;
+  uint8_t* v8;
+  float* q_scale;
+  float* k_scale;
+  uint8_t* v_scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, L, H;
+  int64_t ld_q, ld_k, ld_v;
+};
+
+struct Attn8Args {
+  void* o;
+  float* lse;
+  const int8_t* q8;
+  const int8_t* k8;
+  const uint8_t* v8;
+  const float* q_scale;
+  const float* k_scale;
+  const uint8_t* v_scale;
+  const int32_t* k_lens;
+  int B, L, H;
+  int64_t ld_o;
+  float scale_log2;   // softmax scale * log2(e), fp32
+};
+
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_adaln(const AdaLNArgs& a, hipStream_t s);
 // kind: 0 self-attention, 1 cross-attention, 2 chunk-causal self-attention.
 hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s);
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+hipError_t launch_quant8(const Quant8Args& a, hipStream_t s);
+hipError_t launch_attn8_fwd(const Attn8Args& a, hipStream_t s);
 
 }  // namespace wan

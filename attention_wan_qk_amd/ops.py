@@ -221,3 +221,51 @@ def linear_fwd(x, weight, bias=None, out=None):
                               weight.stride(0), ld_y, _stream(x))
     check("wan_linear_fwd", st)
     return out
+
+
+def quantize_qkv_8bit(q, k, v, heads: int):
+    """INT8 q, k (per 64-token block) and MXFP8 v (per channel and 32 keys) in
+    the layouts the 8-bit attention reads; returns a dict of device tensors."""
+    C = _channels(q)
+    B, L, ld_q = _token_major(q, "q", C)
+    _, Lk, ld_k = _token_major(k, "k", C)
+    _, Lv, ld_v = _token_major(v, "v", C)
+    if Lk != L or Lv != L:
+        raise ValueError("q, k and v must have the same token count")
+    D = C // heads
+    nT = (L + 63) // 64
+    dev = q.device
+    out = {
+        "q8": torch.empty(B, heads, nT, 64, D, dtype=torch.int8, device=dev),
+        "k8": torch.empty(B, heads, nT, 64, D, dtype=torch.int8, device=dev),
+        "v8": torch.empty(B, heads, nT, D, 64, dtype=torch.uint8, device=dev),
+        "q_scale": torch.empty(B, heads, nT, dtype=torch.float32, device=dev),
+        "k_scale": torch.empty(B, heads, nT, dtype=torch.float32, device=dev),
+        "v_scale": torch.empty(B, heads, nT, 2, 32, D // 32, dtype=torch.uint8, device=dev),
+        "B": B, "L": L, "H": heads, "D": D,
+    }
+    st = lib().wan_quantize_qkv_8bit(_ptr(out["q8"]), _ptr(out["k8"]), _ptr(out["v8"]),
+                                     _ptr(out["q_scale"]), _ptr(out["k_scale"]),
+                                     _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v), B, L, heads,
+                                     D, ld_q, ld_k, ld_v, _stream(q))
+    check("wan_quantize_qkv_8bit", st)
+    return out
+
+
+def self_attn_fwd_8bit(qkv8: dict, k_lens=None, scale: float = 0.0, out=None,
+                       return_lse: bool = False):
+    """Self-attention on the output of quantize_qkv_8bit; returns o (and lse)."""
+    B, L, H, D = qkv8["B"], qkv8["L"], qkv8["H"], qkv8["D"]
+    dev = qkv8["q8"].device
+    if out is None:
+        out = torch.empty(B, L, H * D, dtype=torch.bfloat16, device=dev)
+    ld_o = _token_major(out, "out", H * D)[2]
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=dev) if return_lse else None
+    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
+        raise TypeError("k_lens must be a CUDA int32 tensor")
+    st = lib().wan_self_attn_fwd_8bit(_ptr(out), _ptr(lse), _ptr(qkv8["q8"]), _ptr(qkv8["k8"]),
+                                      _ptr(qkv8["v8"]), _ptr(qkv8["q_scale"]),
+                                      _ptr(qkv8["k_scale"]), _ptr(qkv8["v_scale"]), _ptr(k_lens),
+                                      B, L, H, D, ld_o, scale, _stream(out))
+    check("wan_self_attn_fwd_8bit", st)
+    return (out, lse) if return_lse else out

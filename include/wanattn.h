@@ -16,7 +16,8 @@
  *
  * wan_linear_fwd computes the q/k/v and output projections between them
  * (bf16 Linear layers); wan_chunk_causal_attn_fwd is the chunk-wise
- * autoregressive variant of the self-attention.
+ * autoregressive variant of the self-attention; wan_quantize_qkv_8bit and
+ * wan_self_attn_fwd_8bit are its 8-bit (INT8 / FP8) variant.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -263,6 +264,69 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
                            const float* bias, int M, int N, int K,
                            int64_t ld_x, int64_t ld_w, int64_t ld_y,
                            hipStream_t stream);
+
+/*
+ * 8-bit self-attention: wan_quantize_qkv_8bit, then wan_self_attn_fwd_8bit.
+ *
+ * Passage: "论文专题讲解：Wan2.1", inference-optimisation table, row "8-bit
+ * FlashAttention": INT8 for S = Q K^T, FP8 for O = P V, FP32 accumulation
+ * across key blocks. The table gives no granularity; this library takes:
+ *   q, k: symmetric INT8 per (batch, head, block of 64 tokens), fp32 scale
+ *         amax / 127, code = round_half_even(x * (127 / amax)) in fp32,
+ *         clamped to +-127 (amax = 0: codes and scale 0).
+ *   v:    FP8 E4M3 (OCP E4M3FN) per (batch, head, channel, 32 keys) with a
+ *         power-of-two scale 2^e, e = floor(log2 amax) - 8 (OCP microscaling;
+ *         the scale byte is e + 127, amax = 0 gives byte 0), element =
+ *         E4M3(clamp(v / 2^e, +-448)) rounded to nearest even.
+ *   P:    E4M3 of 2^(t - m), t the scaled score in log2 units and m an integer
+ *         running maximum; the softmax denominator sums the unrounded P.
+ * Quantised layouts (nT = ceil(L / 64); rows past L are zero):
+ *   q8, k8   int8  [B][H][nT][64][D]          (token blocks, row-major)
+ *   q_scale, k_scale  fp32 [B][H][nT]
+ *   v8       uint8 [B][H][nT][D][64]          (E4M3, each block transposed)
+ *   v_scale  uint8 [B][H][nT][2][32][D / 32]  (E8M0: [key half][channel % 32]
+ *                                             [channel / 32])
+ * All buffers are caller-owned device memory, 16-byte aligned.
+ */
+
+/*
+ * wan_quantize_qkv_8bit: quantise q, k, v ([B, L, H, D] bf16, row strides
+ * ld_q, ld_k, ld_v; ld = 0 means H*D) into the layouts above. Outputs must
+ * not overlap each other or the inputs. Key lengths play no part.
+ * Errors: WAN_ERROR_INVALID_VALUE for NULL/misaligned pointers, bad sizes or
+ * strides, overlaps; WAN_ERROR_NOT_SUPPORTED for D != 128.
+ */
+wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
+                                  float* q_scale, float* k_scale,
+                                  uint8_t* v_scale, const void* q,
+                                  const void* k, const void* v, int B, int L,
+                                  int H, int D, int64_t ld_q, int64_t ld_k,
+                                  int64_t ld_v, hipStream_t stream);
+
+/*
+ * wan_self_attn_fwd_8bit: self-attention of the quantised q over the
+ * quantised k, v (all L tokens, keys masked by k_lens as in
+ * wan_self_attn_fwd):
+ *   S_ij = sum_d q8_id k8_jd (exact), mult = sq_i sk_j scale log2(e),
+ *   m_i integer, P_ij = E4M3(2^(S_ij mult - m_i)), p_ij the same unrounded,
+ *   o_i = sum_j P_ij v_j / sum_j p_ij  (v dequantised),
+ *   lse_i = ln 2 (m_i + log2 sum_j p_ij).
+ * INT8 MFMA for S, FP8 MFMA with hardware block scales for P V, fp32
+ * accumulation; o is stored as bf16.
+ * o      bf16 [B, L, H, D], row stride ld_o; must not overlap the inputs.
+ * lse    fp32 [B, H, L] or NULL.
+ * k_lens device int32 [B] or NULL (clamped to [0, L]).
+ * softmax_scale  > 0, or <= 0 for 1/sqrt(D).
+ * Errors: WAN_ERROR_INVALID_VALUE (NULL/misaligned pointers, bad sizes,
+ * overlaps), WAN_ERROR_NOT_SUPPORTED (D != 128, or L > 262144).
+ */
+wanStatus_t wan_self_attn_fwd_8bit(void* o, float* lse, const int8_t* q8,
+                                   const int8_t* k8, const uint8_t* v8,
+                                   const float* q_scale, const float* k_scale,
+                                   const uint8_t* v_scale,
+                                   const int32_t* k_lens, int B, int L, int H,
+                                   int D, int64_t ld_o, float softmax_scale,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

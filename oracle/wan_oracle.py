@@ -494,7 +494,7 @@ def quantize_v_mxfp8(v, H: int, block: int = MX_BLOCK):
         blk = vh[:, :, j * block:(j + 1) * block]
         amax = np.abs(blk).max(axis=2)                               # [B, H, d]
         _, fe = np.frexp(np.where(amax > 0, amax, 1.0))
-        ex = np.where(amax > 0, (fe - 1) - 8, -127)
+        ex = np.where(amax > 0, np.maximum((fe - 1) - 8, -127), -127)
         scaled = np.clip(blk / np.ldexp(1.0, ex)[:, :, None, :], -E4M3_MAX, E4M3_MAX)
         c = f64_to_e4m3_bits(scaled)
         codes[:, :, j * block:(j + 1) * block] = c
@@ -517,7 +517,10 @@ def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
 
     q, k, v: [B, L, H*d]. Per (b, h) and query row i, with n = k_len:
       S_ij   = sum_d qc_id kc_jd                    (exact integer dot product)
-      mult   = fp32(fp32(sq_blk(i) sk_blk(j)) c),   c = fp32(scale log2 e)
+      mult   = fp32(fp32(sq_blk(i) sk_blk(j)) c),   c = fp32(scale) * fp32(log2 e) in fp32
+                                                    (scale defaults to 1 / sqrt(d) in fp32),
+               floored at 1e-30 and truncated to 22 significant bits (the reading
+               that lets the INT8 accumulator be read as fp32 without a conversion)
       m_i    = ceil(max_j S_ij mult) - 7            (integer, log2 units)
       t_ij   = fp32 fma(S_ij, mult, -m_i);  p_ij = fp32(2^t_ij);  P_ij = E4M3(p_ij)
       o_i    = sum_j P_ij vdeq_j / sum_j p_ij,   lse_i = ln 2 (m_i + log2 sum_j p_ij)
@@ -530,9 +533,9 @@ def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
     _, _, vdeq = quantize_v_mxfp8(v, H)
     B, _, Lq, d = qc.shape
     Lk = kc.shape[2]
-    if scale is None or scale <= 0:
-        scale = 1.0 / np.sqrt(d)
-    c = np.float32(scale * LOG2E)
+    sc = (np.float32(scale) if scale is not None and scale > 0
+          else np.float32(1) / np.sqrt(np.float32(d)))
+    c = np.float32(sc * np.float32(LOG2E))
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((B, rows.size, H * d))
     lse = np.full((B, H, rows.size), -np.inf)
@@ -543,9 +546,11 @@ def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
         if n == 0:
             continue
         for h in range(H):
-            S = qc[b, h, rows].astype(np.int64) @ kc[b, h, :n].astype(np.int64).T
+            # integer dot products, exact in float64 (|S| < 2^22)
+            S = qc[b, h, rows].astype(np.float64) @ kc[b, h, :n].astype(np.float64).T
             sqk = (sq[b, h, qblk][:, None] * sk[b, h, kblk[:n]][None, :]).astype(np.float32)
-            mult = (sqk * c).astype(np.float32)
+            mult = np.maximum((sqk * c).astype(np.float32), np.float32(1e-30))
+            mult = (mult.view(np.uint32) & np.uint32(0xFFFFFFFC)).view(np.float32)
             m = np.ceil((S * mult.astype(np.float64)).max(axis=1)) - 7
             t = _f32_fma(S.astype(np.float32), mult, -m[:, None])
             p = np.exp2(t.astype(np.float64)).astype(np.float32).astype(np.float64)

@@ -197,3 +197,37 @@ def test_linear_rejections(L):
     assert lin(y=A + MB + 16) == INV   # y overlaps x
     assert lin(b=A + 16) == INV        # bias inside y
     assert lin(lx=1 << 23) == NS       # 256 rows exceed a 32-bit buffer range
+
+
+def test_8bit_rejections(L):
+    def qz(**kw):
+        a = dict(q8=A, k8=A + MB, v8=A + 2 * MB, sq=A + 3 * MB, sk=A + 4 * MB, sv=A + 5 * MB,
+                 q=A + 6 * MB, k=A + 7 * MB, v=A + 8 * MB, B=1, L=100, H=2, D=128, lq=0, lk=0,
+                 lv=0)
+        a.update(kw)
+        return L.wan_quantize_qkv_8bit(a["q8"], a["k8"], a["v8"], a["sq"], a["sk"], a["sv"],
+                                       a["q"], a["k"], a["v"], a["B"], a["L"], a["H"], a["D"],
+                                       a["lq"], a["lk"], a["lv"], None)
+    assert qz(L=0) == OK
+    assert qz(D=64) == NS
+    assert qz(H=0) == INV
+    assert qz(q8=None) == INV
+    assert qz(sk=A + 4 * MB + 4) == INV       # misaligned
+    assert qz(lq=200) == INV                  # row stride < H*D
+    assert qz(k8=A + 16) == INV               # outputs overlap
+    assert qz(q=A + 2 * MB) == INV            # output overlaps an input
+
+    def at(**kw):
+        a = dict(o=A, lse=None, q8=A + MB, k8=A + 2 * MB, v8=A + 3 * MB, sq=A + 4 * MB,
+                 sk=A + 5 * MB, sv=A + 6 * MB, kl=None, B=1, L=100, H=2, D=128, lo=0, scale=0.0)
+        a.update(kw)
+        return L.wan_self_attn_fwd_8bit(a["o"], a["lse"], a["q8"], a["k8"], a["v8"], a["sq"],
+                                        a["sk"], a["sv"], a["kl"], a["B"], a["L"], a["H"], a["D"],
+                                        a["lo"], a["scale"], None)
+    assert at(B=0) == OK
+    assert at(D=256) == NS
+    assert at(o=A + MB) == INV                # o overlaps q8
+    assert at(lse=A + 6 * MB + 8) == INV      # lse inside v_scale
+    assert at(lo=100) == INV
+    assert at(scale=float("nan")) == INV
+    assert at(v8=None) == INV

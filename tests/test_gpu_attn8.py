@@ -1,0 +1,117 @@
+"""8-bit self-attention through the C ABI against the float64 oracle that
+takes the same quantisation decisions: the quantiser's codes and scales
+bit for bit, the attention output within the per-call tolerance save rare
+neighbouring probability codes (tests/_parity.py compare_8bit), on ragged
+shapes, key lengths, peaked logits, zero blocks and the Wan 480p grid
+(sampled rows)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from attention_wan_qk_amd import ops, synth
+from attention_wan_qk_amd.workloads import BY_NAME
+from tests._parity import compare_8bit
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _rand(shape, seed, std=1.0):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
+
+
+def _check_quantised(qz, q, k, v, H):
+    B, L = qz["B"], qz["L"]
+    nT = (L + 63) // 64
+    for name, x in (("q8", q), ("k8", k)):
+        codes, sc = O.quantize_int8_blocks(synth.bf16_bits(x), H)
+        got = qz[name].cpu().numpy().reshape(B, H, nT * 64, -1)
+        assert np.array_equal(got[:, :, :L], codes), name
+        assert not got[:, :, L:].any(), name + " padding"
+        gs = qz["q_scale" if name == "q8" else "k_scale"].cpu().numpy()
+        assert np.array_equal(gs, sc), name + " scales"
+    codes, ex, _ = O.quantize_v_mxfp8(synth.bf16_bits(v), H)
+    got = qz["v8"].cpu().numpy().transpose(0, 1, 2, 4, 3).reshape(B, H, nT * 64, -1)
+    assert np.array_equal(got[:, :, :L], codes), "v8"
+    sv = qz["v_scale"].cpu().numpy()            # [B, H, nT, 2, 32, D/32]
+    D = sv.shape[-1] * 32
+    byt = sv.transpose(0, 1, 2, 3, 5, 4).reshape(B, H, nT * 2, D)
+    nb = ex.shape[2]
+    assert np.array_equal(byt[:, :, :nb].astype(np.int64), ex + 127), "v scales"
+
+
+def _run(name, q, k, v, H, k_lens=None, scale=0.0, rows=None):
+    print(f"[case] attn8 {name}: {tuple(q.shape)} H={H} k_lens={k_lens}", flush=True)
+    qz = ops.quantize_qkv_8bit(q.to(DEV), k.to(DEV), v.to(DEV), H)
+    kl = None if k_lens is None else torch.tensor(k_lens, dtype=torch.int32, device=DEV)
+    o, lse = ops.self_attn_fwd_8bit(qz, k_lens=kl, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    _check_quantised(qz, q, k, v, H)
+    sel = slice(None) if rows is None else torch.as_tensor(rows)
+    ref, rl = O.attention_8bit(synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v), H,
+                               k_lens=k_lens, scale=scale or None, rows=rows)
+    vmax = float(np.abs(O.quantize_v_mxfp8(synth.bf16_bits(v), H)[2]).max())
+    compare_8bit(f"attn8 {name}", synth.bf16_bits(o[:, sel]), ref, vmax)
+    gl = lse[:, :, sel].cpu().numpy().astype(np.float64)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.max(np.abs(gl[fin] - rl[fin]), initial=0.0) < 1e-3
+    return o
+
+
+@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (1, 64, 1), (2, 150, 2), (1, 257, 3), (2, 383, 2),
+                                   (1, 600, 1)])
+def test_attn8_shapes(B, L, H):
+    C = 128 * H
+    q, k, v = (_rand((B, L, C), s) for s in (81, 82, 83))
+    _run(f"{B}x{L}x{H}", q, k, v, H)
+
+
+def test_attn8_key_lengths_and_peaked():
+    B, L, H = 3, 300, 2
+    C = 128 * H
+    q, k, v = (_rand((B, L, C), s, std) for s, std in ((84, 1.0), (85, 1.0), (86, 3.0)))
+    o = _run("k_lens", q, k, v, H, k_lens=[0, 1, 200])
+    assert torch.all(o[0] == 0)
+    _run("peaked", q, k, v, H, scale=4.0 / 128 ** 0.5)
+
+
+def test_attn8_zero_blocks():
+    """All-zero q, k and v blocks (scale 0) next to ordinary ones."""
+    B, L, H = 1, 200, 2
+    C = 128 * H
+    q, k, v = (_rand((B, L, C), s) for s in (87, 88, 89))
+    q[:, :64] = 0
+    k[:, 64:128, :128] = 0
+    v[:, 128:160] = 0
+    _run("zero blocks", q, k, v, H)
+
+
+@pytest.mark.timeout(600)
+def test_attn8_wan_480p_and_bf16_agreement():
+    w = BY_NAME["wan1.3b-480p"]
+    q, k, v = (synth.tensor(w, t, "cpu") for t in ("q", "k", "v"))
+    rows = synth.sample_rows(w)
+    o8 = _run("480p", q, k, v, w.heads, rows=rows)
+    o16 = ops.self_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), w.heads)
+    torch.cuda.synchronize()
+    d = (o8.float() - o16.float()).pow(2).mean().sqrt().item()
+    ref = o16.float().pow(2).mean().sqrt().item()
+    print(f"[attn8] 480p relative RMS difference from the bf16 kernel: {d / ref:.4f}", flush=True)
+    assert d < 0.06 * ref

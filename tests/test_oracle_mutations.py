@@ -49,8 +49,8 @@ MUTATIONS = [
     ("linear bias dropped", "        y = y + _f64(bias)", "        y = y"),
     ("int8 codes truncated", "        c = np.rint((blk * inv[:, :, None, None]).astype(np.float32))",
      "        c = np.trunc((blk * inv[:, :, None, None]).astype(np.float32))"),
-    ("mx scale one binade low", "        ex = np.where(amax > 0, (fe - 1) - 8, -127)",
-     "        ex = np.where(amax > 0, (fe - 1) - 7, -127)"),
+    ("mx scale one binade low", "        ex = np.where(amax > 0, np.maximum((fe - 1) - 8, -127), -127)",
+     "        ex = np.where(amax > 0, np.maximum((fe - 1) - 7, -127), -127)"),
     ("fp8 ties away from zero", "    n = np.rint(a / q)                          # ties to even",
      "    n = np.floor(a / q + 0.5)"),
     ("P left unrounded", "            P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))", "            P = p"),

@@ -578,7 +578,7 @@ def _attention_8bit_loops(q, k, v, H, k_len, scale):
     kc, sk = O.quantize_int8_blocks(k, H)
     _, _, vd = O.quantize_v_mxfp8(v, H)
     B, _, L, d = qc.shape
-    c = np.float32(scale * 1.4426950408889634)
+    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
     out = np.zeros((B, L, H * d))
     for b in range(B):
         for h in range(H):
@@ -586,7 +586,10 @@ def _attention_8bit_loops(q, k, v, H, k_len, scale):
                 ts, mults = [], []
                 for j in range(k_len):
                     s = sum(int(qc[b, h, i, e]) * int(kc[b, h, j, e]) for e in range(d))
-                    mult = np.float32(np.float32(sq[b, h, i // 64] * sk[b, h, j // 64]) * c)
+                    mult = max(np.float32(np.float32(sq[b, h, i // 64] * sk[b, h, j // 64]) * c),
+                               np.float32(1e-30))
+                    mult = np.array([mult], np.float32).view(np.uint32) & np.uint32(0xFFFFFFFC)
+                    mult = mult.view(np.float32)[0]
                     ts.append(s)
                     mults.append(mult)
                 m = math.ceil(max(s * float(mu) for s, mu in zip(ts, mults))) - 7
