@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 / int8 MFMA
 
 
 def parse():
@@ -42,6 +43,9 @@ def parse():
     p.add_argument("--with-projections", action="store_true",
                    help="also time the block with its q/k/v/o and cross projections "
                         "(wan_linear_fwd) included (stderr only)")
+    p.add_argument("--attn8", action="store_true",
+                   help="also time the 8-bit self-attention (quantisation + attention, "
+                        "stderr only)")
     p.add_argument("--chunk-frames", type=int, default=0,
                    help="also time chunk-causal self-attention with chunks of this many "
                         "latent frames (stderr only)")
@@ -155,6 +159,36 @@ def breakdown_projections(args, w, ops, synth, t, per):
                       "projections_tflop": round(total_flop / 1e12, 2),
                       "block_ms_with_projections": round(block_ms, 3)}), file=sys.stderr,
           flush=True)
+
+
+def breakdown_attn8(args, w, ops, q, k, v, o, full_ms):
+    """Time wan_quantize_qkv_8bit and wan_self_attn_fwd_8bit on the step's
+    q, k, v; FLOP counted as for the bf16 call (4 L^2 d H B)."""
+    import torch
+    qz = ops.quantize_qkv_8bit(q, k, v, w.heads)
+    for _ in range(args.warmup):
+        ops.quantize_qkv_8bit(q, k, v, w.heads)
+        ops.self_attn_fwd_8bit(qz, out=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(args.steps):
+        ops.quantize_qkv_8bit(q, k, v, w.heads)
+    ev[1].record()
+    for _ in range(args.steps):
+        ops.self_attn_fwd_8bit(qz, out=o)
+    ev[2].record()
+    torch.cuda.synchronize()
+    qms = ev[0].elapsed_time(ev[1]) / args.steps
+    ams = ev[1].elapsed_time(ev[2]) / args.steps
+    flop = w.self_attn_flop()
+    qbytes = 9 * w.batch * w.tokens * w.dim        # read 3 x 2 B, write 3 x 1 B per element
+    tf = flop / (ams * 1e-3) / 1e12
+    print(json.dumps({"attn8": {
+        "quantize_ms": round(qms, 3), "quantize_gbs": round(qbytes / (qms * 1e-3) / 1e9, 1),
+        "attn_ms": round(ams, 3), "tflops_effective": round(tf, 1),
+        "frac_of_8bit_peak": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+        "speedup_vs_bf16_incl_quantize": round(full_ms / (qms + ams), 3)}}), file=sys.stderr,
+        flush=True)
 
 
 def breakdown_causal(args, w, ops, q, k, v, o, full_ms):
@@ -287,6 +321,9 @@ def main():
 
     if args.with_projections:
         breakdown_projections(args, w, ops, synth, t, per)
+
+    if args.attn8:
+        breakdown_attn8(args, w, ops, qr, kr, t["v"], o, per["self_attn"])
 
     if args.chunk_frames > 0:
         breakdown_causal(args, w, ops, qr, kr, t["v"], o, per["self_attn"])
