@@ -307,7 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     const float mt = mx * a.scale_log2;
     if (__any(mt > m_used + kRescaleThreshold)) {
       const float mn = fmaxf(m_used, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
+      // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
+      const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ls[i] *= alpha;
 #pragma unroll
