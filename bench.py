@@ -107,13 +107,29 @@ def cpu_baseline(w, tensors, budget_s: float):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    rate = flop / dt
+    # one (batch, head) pair on a single thread
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        sl = slice(0, d)
+        qb = synth.bf16_bits(q[0, rows[:128], sl])
+        kb, vb = synth.bf16_bits(k[0, :, sl]), synth.bf16_bits(v[0, :, sl])
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            O.attention(qb, kb, vb, w.tokens, 1.0 / np.sqrt(d))
+            single = 4.0 * 128 * w.tokens * d / (time.perf_counter() - t1) / 1e12
+    except Exception:  # pragma: no cover
+        pass
     return {
-        "value": flop / dt / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"self-attention of {len(rows)} query rows x {pairs} (batch, head) pairs of "
                   f"{w.name} (L={w.tokens}), float64 NumPy, {dt:.1f} s incl. host copies",
+        "full_problem_s_extrapolated": round(w.self_attn_flop() / rate, 1),
+        "single_thread_tflops": None if single is None else round(single, 5),
     }
 
 
@@ -301,14 +317,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    per = {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
-           for i, n in enumerate(names)}
+    times = {n: sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+             for i, n in enumerate(names)}
+    per = {n: sum(ts) / len(ts) for n, ts in times.items()}
 
     attn_flop = w.self_attn_flop()
     attn_tflops = attn_flop / (per["self_attn"] * 1e-3) / 1e12
     breakdown = {}
     for n in names:
-        rec = {"ms": round(per[n], 4)}
+        ts = times[n]
+        rec = {"ms": round(per[n], 4), "median_ms": round(ts[len(ts) // 2], 4),
+               "min_ms": round(ts[0], 4)}
         if n == "self_attn":
             rec.update(tflops=round(attn_tflops, 1), frac_mfma=round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4))
         elif n == "cross_attn":
