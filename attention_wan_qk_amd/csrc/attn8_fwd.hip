@@ -29,7 +29,9 @@
 //    V^T fragments straight from the transposed tile, P from the softmax
 //    registers (v_cvt_pk_fp8_f32, round to nearest even), the V block scales
 //    applied by the MFMA itself (one E8M0 byte per lane, selected by op_sel).
-//  * The row sum l accumulates the fp32 P before rounding.
+//  * The row sum l is the sum of the rounded P, formed by one more FP8 MFMA
+//    per tile (an all-ones A operand against P) instead of 32 VALU additions
+//    per lane: the softmax phase, not the MFMA pipe, bounds this kernel.
 #include "wan_device.h"
 #include "wan_internal.h"
 
@@ -187,7 +189,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m_used = -INFINITY;
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 lacc;                                // row sums of P (every element of a lane)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lacc[v] = 0.f;
+  // E4M3 1.0 in every byte: the A operand that turns the P V product into row sums
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
   i32x16 s[2];
   i32x8 pq;                                   // P of the tile as 32 E4M3 bytes
 
@@ -209,6 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
                                                                0, 127);                      \
   }
       WAN_PV(0) WAN_PV(1) WAN_PV(2) WAN_PV(3)
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pq, lacc, 0, 0, 0, 127, 0, 127);
 #undef WAN_PV
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
 #pragma unroll
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 3, 0);
     }
     if (jj < nT) {
       const char* Kt = Ks + KS * kKTile;
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
       const float mn = fmaxf(m_used, ceilf(mt) - 7.0f);
       const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ls[i] *= alpha;
+      for (int v = 0; v < 16; ++v) lacc[v] *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -291,7 +299,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + e], mult, cc));
-        ls[e] += p[e];
       }
       uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       pq[q4] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
@@ -334,12 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
     phase_barrier();
   }
 
-  float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
-                                                     false, false);
-    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
+  const float lsum = lacc[0];
   if (qrow < a.L) {
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.L + qrow) * a.ld_o + h * kHD;

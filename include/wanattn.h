@@ -279,7 +279,7 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
  *         the scale byte is e + 127, amax = 0 gives byte 0), element =
  *         E4M3(clamp(v / 2^e, +-448)) rounded to nearest even.
  *   P:    E4M3 of 2^(t - m), t the scaled score in log2 units and m an integer
- *         running maximum; the softmax denominator sums the unrounded P.
+ *         running maximum; the softmax denominator sums the rounded P.
  * Quantised layouts (nT = ceil(L / 64); rows past L are zero):
  *   q8, k8   int8  [B][H][nT][64][D]          (token blocks, row-major)
  *   q_scale, k_scale  fp32 [B][H][nT]
@@ -308,9 +308,9 @@ wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
  * quantised k, v (all L tokens, keys masked by k_lens as in
  * wan_self_attn_fwd):
  *   S_ij = sum_d q8_id k8_jd (exact), mult = sq_i sk_j scale log2(e),
- *   m_i integer, P_ij = E4M3(2^(S_ij mult - m_i)), p_ij the same unrounded,
- *   o_i = sum_j P_ij v_j / sum_j p_ij  (v dequantised),
- *   lse_i = ln 2 (m_i + log2 sum_j p_ij).
+ *   m_i integer, P_ij = E4M3(2^(S_ij mult - m_i)),
+ *   o_i = sum_j P_ij v_j / sum_j P_ij  (v dequantised),
+ *   lse_i = ln 2 (m_i + log2 sum_j P_ij).
  * INT8 MFMA for S, FP8 MFMA with hardware block scales for P V, fp32
  * accumulation; o is stored as bf16.
  * o      bf16 [B, L, H, D], row stride ld_o; must not overlap the inputs.

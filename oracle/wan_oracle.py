@@ -406,7 +406,7 @@ def linear(x, w, bias=None) -> np.ndarray:
 # channel, block of 32 keys) with a power-of-two (E8M0) scale, the OCP
 # microscaling recipe; P is rounded to FP8 E4M3 after the row maximum (an
 # integer in log2 units) is subtracted, and the softmax denominator sums the
-# unrounded P. Every quantised code is decided in fp32, as the kernel decides
+# rounded P (so the weights applied to v sum to one). Every quantised code is decided in fp32, as the kernel decides
 # it (numpy float32 arithmetic is IEEE-correctly rounded, like the GPU's).
 INT8_BLOCK = 64
 MX_BLOCK = 32
@@ -523,7 +523,7 @@ def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
                that lets the INT8 accumulator be read as fp32 without a conversion)
       m_i    = ceil(max_j S_ij mult) - 7            (integer, log2 units)
       t_ij   = fp32 fma(S_ij, mult, -m_i);  p_ij = fp32(2^t_ij);  P_ij = E4M3(p_ij)
-      o_i    = sum_j P_ij vdeq_j / sum_j p_ij,   lse_i = ln 2 (m_i + log2 sum_j p_ij)
+      o_i    = sum_j P_ij vdeq_j / sum_j P_ij,   lse_i = ln 2 (m_i + log2 sum_j P_ij)
     Returns o [B, rows, H*d] and lse [B, H, rows]; n = 0 gives o = 0,
     lse = -inf. The integer offset m_i only moves P by a power of two, which
     leaves every normal E4M3 rounding unchanged.
@@ -555,7 +555,7 @@ def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
             t = _f32_fma(S.astype(np.float32), mult, -m[:, None])
             p = np.exp2(t.astype(np.float64)).astype(np.float32).astype(np.float64)
             P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))
-            l = p.sum(axis=1)
+            l = P.sum(axis=1)
             o[b, :, h * d:(h + 1) * d] = (P @ vdeq[b, h, :n]) / l[:, None]
             lse[b, h] = np.log(2.0) * (m + np.log2(l))
     return o, lse

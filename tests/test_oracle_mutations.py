@@ -54,7 +54,7 @@ MUTATIONS = [
     ("fp8 ties away from zero", "    n = np.rint(a / q)                          # ties to even",
      "    n = np.floor(a / q + 0.5)"),
     ("P left unrounded", "            P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))", "            P = p"),
-    ("denominator of rounded P", "            l = p.sum(axis=1)", "            l = P.sum(axis=1)"),
+    ("denominator of unrounded p", "            l = P.sum(axis=1)", "            l = p.sum(axis=1)"),
 ]
 
 

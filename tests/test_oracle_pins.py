@@ -600,7 +600,7 @@ def _attention_8bit_loops(q, k, v, H, k_len, scale):
                     p = float(np.float32(2.0 ** float(t)))
                     P = float(O.e4m3_bits_to_f64(O.f64_to_e4m3_bits(p)))
                     num += P * vd[b, h, j]
-                    den += p
+                    den += P
                 out[b, i, h * d:(h + 1) * d] = num / den
     return out
 
@@ -621,7 +621,8 @@ def test_attention_8bit_properties():
     ex, exl = O.self_attention(q, k, v, H)
     assert np.sqrt(np.mean((o - ex) ** 2)) < 0.06 * np.sqrt(np.mean(ex ** 2))
     # against exact attention on the dequantised operands, only P's rounding differs:
-    # |o - o'| <= 2^-4 max|v| + (keys) 2^-10 max|v| / sum p
+    # each weight moves by at most 2^-4 of itself (normal) or 2^-10 (subnormal), in the
+    # numerator and the denominator alike
     qc, sq = O.quantize_int8_blocks(q, H)
     kc, sk = O.quantize_int8_blocks(k, H)
     _, _, vd = O.quantize_v_mxfp8(v, H)
@@ -633,7 +634,8 @@ def test_attention_8bit_properties():
             w = np.exp(S - S.max(axis=1, keepdims=True))
             od = (w @ vd[b, h]) / w.sum(axis=1, keepdims=True)
             vmax = np.abs(vd[b, h]).max()
-            assert np.all(np.abs(o[b, :, h * d:(h + 1) * d] - od) <= (2 ** -4 + L * 2 ** -10) * vmax)
+            assert np.all(np.abs(o[b, :, h * d:(h + 1) * d] - od)
+                          <= 2 * (2 ** -4 + L * 2 ** -10) * vmax)
     # all logits equal (q = 0): p = 2^7 exactly for every key, so o is the mean of the
     # dequantised values
     oz, lz = O.attention_8bit(np.zeros_like(q), k, v, H)
@@ -641,6 +643,11 @@ def test_attention_8bit_properties():
         assert np.allclose(oz[:, :, h * d:(h + 1) * d], vd[:, h].mean(axis=1, keepdims=True),
                            rtol=0, atol=1e-12)
     assert np.allclose(lz, np.log(L))
+    # a single visible key returns its dequantised value exactly
+    o1k, _ = O.attention_8bit(q, k, v, H, k_lens=[1, 1])
+    for h in range(H):
+        assert np.array_equal(o1k[:, :, h * d:(h + 1) * d],
+                              np.broadcast_to(vd[:, h, :1], (B, L, d)))
     # key lengths: k_len 0 gives zeros and -inf; keys in blocks wholly past k_len do nothing
     o0, l0 = O.attention_8bit(q, k, v, H, k_lens=[0, 128])
     assert not o0[0].any() and np.all(np.isneginf(l0[0]))
