@@ -223,9 +223,10 @@ def linear_fwd(x, weight, bias=None, out=None):
     return out
 
 
-def quantize_qkv_8bit(q, k, v, heads: int):
+def quantize_qkv_8bit(q, k, v, heads: int, out: dict | None = None):
     """INT8 q, k (per 64-token block) and MXFP8 v (per channel and 32 keys) in
-    the layouts the 8-bit attention reads; returns a dict of device tensors."""
+    the layouts the 8-bit attention reads; returns a dict of device tensors
+    (``out``, a dict returned by an earlier call of the same shape, is reused)."""
     C = _channels(q)
     B, L, ld_q = _token_major(q, "q", C)
     _, Lk, ld_k = _token_major(k, "k", C)
@@ -235,6 +236,15 @@ def quantize_qkv_8bit(q, k, v, heads: int):
     D = C // heads
     nT = (L + 63) // 64
     dev = q.device
+    if out is not None:
+        if (out["B"], out["L"], out["H"], out["D"]) != (B, L, heads, D):
+            raise ValueError("out was made for another shape")
+        st = lib().wan_quantize_qkv_8bit(_ptr(out["q8"]), _ptr(out["k8"]), _ptr(out["v8"]),
+                                         _ptr(out["q_scale"]), _ptr(out["k_scale"]),
+                                         _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v), B, L,
+                                         heads, D, ld_q, ld_k, ld_v, _stream(q))
+        check("wan_quantize_qkv_8bit", st)
+        return out
     out = {
         "q8": torch.empty(B, heads, nT, 64, D, dtype=torch.int8, device=dev),
         "k8": torch.empty(B, heads, nT, 64, D, dtype=torch.int8, device=dev),
