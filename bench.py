@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--with-projections", action="store_true",
                    help="also time the block with its q/k/v/o and cross projections "
                         "(wan_linear_fwd) included (stderr only)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the tiny workload's step eagerly and as a replayed HIP "
+                        "graph (launch overhead; stderr only)")
     p.add_argument("--attn8", action="store_true",
                    help="also time the 8-bit self-attention (quantisation + attention, "
                         "stderr only)")
@@ -176,6 +179,63 @@ def breakdown_projections(args, w, ops, synth, t, per):
                       "projections_tflop": round(total_flop / 1e12, 2),
                       "block_ms_with_projections": round(block_ms, 3)}), file=sys.stderr,
           flush=True)
+
+
+def graph_launch_overhead(ops, synth, n: int = 200):
+    """The tiny workload's sublayer step (8 launches) is launch-bound: time it
+    eagerly and as a captured, replayed HIP graph."""
+    import torch
+    from attention_wan_qk_amd.workloads import BY_NAME
+    w = BY_NAME["tiny-5x8x8"]
+    dev = "cuda:0"
+    B, L, C, H, Lt = w.batch, w.tokens, w.dim, w.heads, w.text_len
+    t = {k: synth.tensor(w, k, dev) for k in
+         ("x", "y", "q", "k", "v", "text_k", "text_v", "cross_q", "cross_y", "gain_q",
+          "gain_k", "gain_cq", "gain_ck", "mod")}
+    e = t["mod"]
+    emp = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+    h1, qr, kr, o, x2, h3, cq, ck, oc, x3 = (emp(B, L, C) for _ in range(10))
+    ck = emp(B, Lt, C)
+
+    def step():
+        ops.adaln_modulate_gate(t["x"], None, None, e[:, 0], e[:, 1], w.eps, want_x=False,
+                                h_out=h1)
+        ops.qk_norm_rope3d(t["q"], t["k"], H, w.grid, t["gain_q"], t["gain_k"], eps=w.eps,
+                           q_out=qr, k_out=kr)
+        ops.self_attn_fwd(qr, kr, t["v"], H, out=o)
+        ops.adaln_modulate_gate(t["x"], t["y"], e[:, 2], None, None, w.eps, x_out=x2, h_out=h3)
+        ops.qk_norm_rope3d(t["cross_q"], None, H, None, t["gain_cq"], eps=w.eps, rope=False,
+                           q_out=cq)
+        ops.qk_norm_rope3d(None, t["text_k"], H, None, None, t["gain_ck"], eps=w.eps,
+                           rope=False, k_out=ck)
+        ops.cross_attn_fwd(cq, ck, t["text_v"], H, out=oc)
+        ops.adaln_modulate_gate(x2, t["cross_y"], None, None, None, w.eps, want_h=False,
+                                x_out=x3)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / n
+
+    eager_us = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    graph_us = timed(g.replay)
+    print(json.dumps({"graph": {"workload": w.name, "launches_per_step": 8,
+                                "eager_us_per_step": round(eager_us, 1),
+                                "graph_us_per_step": round(graph_us, 1)}}),
+          file=sys.stderr, flush=True)
 
 
 def breakdown_attn8(args, w, ops, q, k, v, o, full_ms):
@@ -341,6 +401,9 @@ def main():
 
     if args.with_projections:
         breakdown_projections(args, w, ops, synth, t, per)
+
+    if args.graph:
+        graph_launch_overhead(ops, synth)
 
     if args.attn8:
         breakdown_attn8(args, w, ops, qr, kr, t["v"], o, per["self_attn"])
