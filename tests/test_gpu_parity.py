@@ -214,6 +214,29 @@ def test_adaln_per_token_modulation_and_inplace():
     compare("per-token h", synth.bf16_bits(ho), h)
 
 
+@pytest.mark.parametrize("per_token", [False, True])
+def test_adaln_row_pairs_across_samples(per_token):
+    """Without a residual input a wavefront owns two consecutive token rows.
+    With an odd L one pair holds the last row of sample 0 and the first of
+    sample 1 (different modulation vectors), and the odd total leaves a single
+    row at the end; h is written in place over x."""
+    _announce(f"adaln row pairs, per_token={per_token}")
+    B, L, C = 3, 37, 1536
+    x = _rand((B, L, C), 31).to(DEV)
+    shape = (B, L, 6, C) if per_token else (B, 6, C)
+    e = (torch.randn(*shape, generator=torch.Generator().manual_seed(6)) * 0.3).float()
+    ed = e.to(DEV)
+    pick = (lambda t, i: t[:, :, i]) if per_token else (lambda t, i: t[:, i])
+    xb = synth.bf16_bits(x)
+    x_work = x.clone()
+    _, ho = ops.adaln_modulate_gate(x_work, None, None, pick(ed, 0), pick(ed, 1), 1e-6,
+                                    want_x=False, h_out=x_work)
+    torch.cuda.synchronize()
+    en = e.numpy().astype(np.float64)
+    _, h = O.adaln_modulate_gate(xb, None, None, pick(en, 0), pick(en, 1), 1e-6)
+    compare(f"row pairs h (per_token={per_token})", synth.bf16_bits(ho), h)
+
+
 def test_determinism_and_side_stream():
     _announce("determinism + side stream")
     w = WORKLOADS[0]
