@@ -23,14 +23,20 @@
 //    wave feeding the MFMA pipe while the other runs the softmax on the VALU.
 //  * Inside a GEMM phase the LDS operand reads are issued a few fragments
 //    ahead of their MFMAs (scheduling groups), hiding LDS latency.
-//  * The running max is in log2 units of the scaled scores; it is only moved
-//    (and O, l rescaled) when some row's tile max exceeds it by more than 8,
-//    so the exponentials stay <= 2^8 and the rescale is rare.
-//  * K/V tiles are double-buffered in LDS and loaded by the waves of group 0
-//    with buffer loads whose destination is the LDS (no register staging):
-//    issued right after their GEMM phase (once its LDS reads are done), they
-//    complete during the following softmax phase, which reads no LDS. Rows
-//    past k_len fall outside the buffer resource and read as zero. Each
+//  * The running max m is in log2 units of the scaled scores and is only
+//    moved (O and l rescaled) when a row's tile max exceeds it by more than
+//    8, so every P stays <= 2^8 and the rescale is rare. The tile max itself
+//    is only formed on a row's first tile and when a lane's sum of P over
+//    the tile (32 values) exceeds 2^8, which any exponent above 8 causes;
+//    such a tile is recomputed after the rescale. The softmax phase is
+//    otherwise one fma, one exp2 and one add per score and the bf16
+//    conversion.
+//  * K/V tiles are double-buffered in LDS and moved by buffer loads whose
+//    destination is the LDS (no register staging), issued at the start of a
+//    softmax phase (which reads no LDS) and awaited at its end: group 1
+//    loads the next K tile, group 0 the next V tile, so neither group's
+//    phase carries all the load issue. Rows past k_len fall outside the
+//    buffer resource and read as zero. Each
 //    16-byte chunk of a row is XOR-swizzled so the MFMA operand reads are
 //    bank-conflict free; a load writes 16 bytes per lane at base + 16 lane,
 //    so each lane fetches the global chunk that belongs there.
@@ -57,8 +63,9 @@ constexpr int kHD = 128;                     // head size
 constexpr int kRowBytes = kHD * 2;
 constexpr int kTileBytes = kBN * kRowBytes;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLoadsPerWave = kTileBytes / 1024 / (kWaves / 2);  // group-0 waves, 1 KiB each
+constexpr int kLoadsPerWave = kTileBytes / 1024 / (kWaves / 2);  // per tile and wave of a group, 1 KiB each
 constexpr float kRescaleThreshold = 8.0f;    // log2 units
+constexpr float kSumLimit = 256.0f;          // per-lane tile sum of P that forces the tile max
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -76,8 +83,8 @@ struct Int {
 constexpr int kWaitLoads = 0x0F70;
 
 // Barrier between phases, without a memory fence. The only LDS writes inside
-// the main loop are the group-0 buffer loads into LDS; their waves wait for
-// them (kWaitLoads) before the barrier that publishes them. Every LDS read of
+// the main loop are the buffer loads into LDS; the waves that issue them wait
+// for them (kWaitLoads) before the barrier that publishes them. Every LDS read of
 // a phase feeds an MFMA issued before that phase's barrier, so it has
 // completed. The empty asm statements keep the compiler from moving memory
 // accesses across the barrier.
@@ -152,9 +159,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
 
-  // The waves of group 0 move the K and V tiles from global memory straight
+  // The four waves of a group move a K or V tile from global memory straight
   // into LDS (buffer loads with the LDS as destination). Load i of wave w
-  // fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
+  // (w = wave % 4) fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
   // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so it fetches the
   // logical chunk (l % 16) ^ swizzle of that row.
   uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
@@ -292,81 +299,101 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
           if (key >= lim_row) s[kb][v] = -INFINITY;
         }
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
+    // P = 2^(s c - m) and its per-lane partial sums
+    float sg[4];
+    auto exps = [&]() __attribute__((always_inline)) {
+      const float neg_m = -m_used;
 #pragma unroll
-    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+      for (int i = 0; i < 4; ++i) sg[i] = 0.f;
 #pragma unroll
-    for (int kb = 1; kb < kKB; ++kb)
+      for (int kc = 0; kc < kKC; ++kc) {
+        float p[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * a.scale_log2;
-    if (__any(mt > m_used + kRescaleThreshold)) {
-      const float mn = fmaxf(m_used, mt);
-      // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
-      const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ls[i] *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
-      m_used = mn;
-    }
-    const float neg_m = -m_used;
-#pragma unroll
-    for (int kc = 0; kc < kKC; ++kc) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
-        ls[e & 3] += p[e];
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
+          sg[e & 3] += p[e];
+        }
+        f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
+        pf[kc] = __builtin_convertvector(pv, bf16x8);
       }
-      f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
-      pf[kc] = __builtin_convertvector(pv, bf16x8);
+    };
+    bool exact = __any(m_used == -INFINITY);
+    if (!exact) {
+      exps();
+      const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));
+      exact = __any(!(big <= kSumLimit));
     }
+    if (exact) {
+      float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+#pragma unroll
+      for (int kb = 1; kb < kKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mt = mx * a.scale_log2;
+      if (__any(mt > m_used + kRescaleThreshold)) {
+        const float mn = fmaxf(m_used, mt);
+        // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
+        const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ls[i] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+        m_used = mn;
+      }
+      exps();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ls[i] += sg[i];
   };
 
   // Two groups of waves run the same phase sequence, group 1 one interval
   // behind group 0, so that in every interval one wave of each SIMD is in a
   // GEMM phase (MFMA) while the other is in a softmax phase (VALU):
   //   phase 2j: GEMM(j) = PV(j-1) + S(j);   phase 2j+1: softmax(j).
-  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1.
-  // Group 0 loads K(j+1) and V(j) into the slots freed by K(j-1) and V(j-2)
-  // right after its GEMM phase of interval 2j and waits for them at the end
-  // of interval 2j+1, before the barrier that publishes them.
+  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
+  // slots of K(j-1) and V(j-2) are free from interval 2j on (their last
+  // reader, group 1's GEMM(j-1), ran in interval 2j-1). Group 1 loads K(j+1)
+  // during its softmax phase of interval 2j, group 0 loads V(j) during its
+  // softmax phase of interval 2j+1; each waits for its loads at the end of
+  // that phase, before the barrier that publishes them, and both are in
+  // place for group 0's GEMM(j+1) in interval 2j+2.
   const int nIntervals = 2 * nT + 2;
   for (int i = 0; i < nIntervals; i += 4) {
     const int j0 = i >> 1;
-    if (group == 0) {
-      gemm(Int<0>{}, j0);
-      if (j0 < nT) {
-        if (j0 + 1 < nT) dma_k(j0 + 1, 1);
-        dma_v(j0, 0);
-      }
-    } else softmax(j0 - 1);
+    if (group == 0) gemm(Int<0>{}, j0);
+    else {
+      if (j0 + 1 < nT) dma_k(j0 + 1, 1);
+      softmax(j0 - 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
+    }
     phase_barrier();
     if (group == 0) {
+      if (j0 < nT) dma_v(j0, 0);
       softmax(j0);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);   // this wave's tile loads landed
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
     } else gemm(Int<0>{}, j0);
     phase_barrier();
     const int j1 = j0 + 1;
-    if (group == 0) {
-      gemm(Int<1>{}, j1);
-      if (j1 < nT) {
-        if (j1 + 1 < nT) dma_k(j1 + 1, 0);
-        dma_v(j1, 1);
-      }
-    } else softmax(j0);
+    if (group == 0) gemm(Int<1>{}, j1);
+    else {
+      if (j1 + 1 < nT) dma_k(j1 + 1, 0);
+      softmax(j0);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
+    }
     phase_barrier();
     if (group == 0) {
+      if (j1 < nT) dma_v(j1, 1);
       softmax(j1);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);   // this wave's tile loads landed
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
     } else gemm(Int<1>{}, j1);
     phase_barrier();
   }
