@@ -53,10 +53,7 @@ constexpr int kWaves = 8;                    // two groups of four, one wave of 
 constexpr int kAheadV = 4;                   // V fragments read ahead of their MFMAs
 constexpr int kAheadK = 4;                   // K fragments read ahead of their MFMAs
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
-#ifndef WAN_ATTN_BN
-#define WAN_ATTN_BN 64
-#endif
-constexpr int kBN = WAN_ATTN_BN;             // keys per tile
+constexpr int kBN = 64;                      // keys per tile
 constexpr int kKB = kBN / 32;                // 32-key blocks per tile
 constexpr int kKC = kBN / 16;                // 16-key chunks per tile (PV k-steps)
 constexpr int kHD = 128;                     // head size
