@@ -11,9 +11,11 @@
 //
 // Memory-bound: one wavefront owns one token row (q and k), streams it as
 // 16-byte vectors held in registers, reduces the sum of squares across the
-// wave and writes the rotated row back. Every lane works on the same 4 pairs
-// of every head it touches (its chunks are lane + 64 i and a head is 16
-// chunks), so its 4 (cos, sin) pairs are computed once per token.
+// wave and writes the rotated row back; the fp32 gain of the next 8-channel
+// chunk is requested before the current chunk is written. Every lane works
+// on the same 4 pairs of every head it touches (its chunks are lane + 64 i
+// and a head is 16 chunks), so its 4 (cos, sin) pairs are computed once per
+// token.
 #include "wan_device.h"
 #include "wan_internal.h"
 #include "../../include/wanattn.h"
@@ -61,34 +63,45 @@ __device__ __forceinline__ void norm_rope_one(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) scale[i] = 1.0f;
   }
+  // The gain of chunk i + 1 is requested before chunk i is written, so the
+  // L2 latency of the gain vectors is not paid chunk by chunk. Without a gain
+  // (or without the norm) the factor is 1.
+  const bool use_gain = norm && gain;
+  auto load_gain = [&](int c, float* g) __attribute__((always_inline)) {
+    if (use_gain && c < nchunk) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + 8 * c);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + 8 * c + 4);
+      g[0] = g0[0]; g[1] = g0[1]; g[2] = g0[2]; g[3] = g0[3];
+      g[4] = g1[0]; g[5] = g1[1]; g[6] = g1[2]; g[7] = g1[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = 1.0f;
+    }
+  };
+  float g_n[8];
+  load_gain(lane, g_n);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + kWave * i;
-    if (c >= nchunk) continue;
-    float f[8];
-    unpack8(v[i], f);
-    if (norm) {
-      if (gain) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + 8 * c);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + 8 * c + 4);
-        f[0] *= scale[i] * g0[0]; f[1] *= scale[i] * g0[1];
-        f[2] *= scale[i] * g0[2]; f[3] *= scale[i] * g0[3];
-        f[4] *= scale[i] * g1[0]; f[5] *= scale[i] * g1[1];
-        f[6] *= scale[i] * g1[2]; f[7] *= scale[i] * g1[3];
-      } else {
+    float g[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= scale[i];
-      }
-    }
-    if (rope) {
+    for (int e = 0; e < 8; ++e) g[e] = g_n[e];
+    if (i + 1 < NCH) load_gain(c + kWave, g_n);
+    if (c < nchunk) {
+      float f[8];
+      unpack8(v[i], f);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float re = f[2 * p], im = f[2 * p + 1];
-        f[2 * p] = re * cs[p] - im * sn[p];
-        f[2 * p + 1] = re * sn[p] + im * cs[p];
+      for (int e = 0; e < 8; ++e) f[e] *= scale[i] * g[e];
+      if (rope) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float re = f[2 * p], im = f[2 * p + 1];
+          f[2 * p] = re * cs[p] - im * sn[p];
+          f[2 * p + 1] = re * sn[p] + im * cs[p];
+        }
       }
+      store_stream(dst + 8 * c, pack8(f));
     }
-    store_stream(dst + 8 * c, pack8(f));
   }
 }
 
