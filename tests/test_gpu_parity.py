@@ -214,6 +214,40 @@ def test_adaln_per_token_modulation_and_inplace():
     compare("per-token h", synth.bf16_bits(ho), h)
 
 
+@pytest.mark.parametrize("pattern", ["rising", "falling", "spike", "sawtooth"])
+def test_self_attn_running_max_paths(pattern):
+    """Logits whose tile maxima follow a set pattern across the 12 key tiles
+    of a 768-token sequence. The kernel keeps the running max m lazily: a
+    tile's max is only formed on a row's first tile and when a lane's sum of
+    P exceeds 2^8. 'rising' (+~10 in log2 units per tile) moves m on every
+    tile, 'falling' never after the first (later tiles underflow), 'spike'
+    puts one key 20 above the rest in tile 6, 'sawtooth' alternates."""
+    _announce(f"self_attn running-max pattern {pattern}")
+    rng = np.random.default_rng({"rising": 1, "falling": 2, "spike": 3, "sawtooth": 4}[pattern])
+    L, d = 768, 128
+    u = rng.choice([-1.0, 1.0], size=d)               # |u|^2 = 128: q.k ~ 128 c per unit of c
+    q = u[None, :] + 0.05 * rng.standard_normal((L, d))
+    tile = np.arange(L) // 64
+    # c per key: log2-unit logit of a key is about 16.3 c at scale 1/sqrt(d)
+    if pattern == "rising":
+        c = 0.6 * tile
+    elif pattern == "falling":
+        c = 0.6 * (11 - tile)
+    elif pattern == "spike":
+        c = np.zeros(L)
+        c[6 * 64 + 17] = 1.25
+    else:
+        c = np.where(tile % 2 == 0, 0.0, 0.9)
+    k = c[:, None] * u[None, :] + 0.3 * rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    qt, kt, vt = (torch.from_numpy(x[None].astype(np.float32)).to(torch.bfloat16)
+                  for x in (q, k, v))
+    o = ops.self_attn_fwd(qt.to(DEV), kt.to(DEV), vt.to(DEV), 1)
+    torch.cuda.synchronize()
+    ref, _ = O.self_attention(*(synth.bf16_bits(t) for t in (qt, kt, vt)), 1)
+    compare(f"running max {pattern}", synth.bf16_bits(o), ref)
+
+
 @pytest.mark.parametrize("per_token", [False, True])
 def test_adaln_row_pairs_across_samples(per_token):
     """Without a residual input a wavefront owns two consecutive token rows.
