@@ -13,9 +13,14 @@
 //    wavefronts (2 along tokens x 4 along features, 128 x 64 each: 8
 //    accumulator tiles of 32 x 32 per wave, two waves per SIMD).
 //  * K advances in steps of 64 through a double-buffered LDS stage (x and W
-//    tiles, 32 KiB each). The global loads of step k+1 are issued before the
-//    MFMAs of step k and written to the other LDS buffer after them: one
-//    barrier per step.
+//    tiles, 32 KiB each). The tiles of step k+1 are moved by buffer loads
+//    whose destination is the LDS (no register staging), issued before the
+//    MFMAs of step k into the other buffer; each wave waits for its own
+//    loads before the step's barrier, which publishes them: one barrier per
+//    step. The two buffers are reached through restrict pointers of an
+//    inlined step function, so the compiler can tell that the loads in
+//    flight do not write what the step's LDS reads read, and places no wait
+//    before those reads.
 //  * Each 16-byte chunk c of tile row r is stored at chunk c ^ ((r / 2) % 8),
 //    so the 16 rows read together at one logical chunk by half a wave fall
 //    into 16 different 16-byte bank groups.
@@ -38,23 +43,42 @@ constexpr int kBK = 64;                  // K per LDS stage
 constexpr int kThreads = 512;
 constexpr int kRowBytes = kBK * 2;       // 128
 constexpr int kTileBytes = kBM * kRowBytes;  // 32 KiB (x and W tiles are the same size)
-constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per tile: 4
+constexpr int kLoads = kTileBytes / 16 / kThreads;  // 1 KiB loads per wave per tile: 4
 constexpr int kGroupM = 4;               // token tiles per band
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ int chunk_phys(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__device__ __forceinline__ bf16x8 lds_read16(const char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+__device__ __forceinline__ bf16x8 lds_read16(const lds_char* p) {
+  return *reinterpret_cast<const lds_bf16x8*>(p);
+}
+
+// One K step: the loads of the next stage go to (xn, wn) while the MFMAs read
+// the current stage (xc, wc). The four LDS pointers are restrict parameters of
+// an inlined function, so the compiler knows the loads in flight do not write
+// what the reads below read and needs no wait before them.
+template <typename Dma, typename Mma>
+__device__ __forceinline__ void k_step(int kt, bool more, const lds_char* __restrict__ xc,
+                                       const lds_char* __restrict__ wc, lds_char* __restrict__ xn,
+                                       lds_char* __restrict__ wn, Dma& dma, Mma& mma) {
+  if (more) dma(kt + 1, xn, wn);
+  mma(xc, wc);
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
-  char* const Ws = smem;                    // W tiles, buffers 0 and 1
-  char* const Xs = smem + 2 * kTileBytes;   // x tiles, buffers 0 and 1
+  __shared__ __attribute__((aligned(1024))) char smem_w0[kTileBytes], smem_w1[kTileBytes],
+      smem_x0[kTileBytes], smem_x1[kTileBytes];
+  lds_char* const W0 = (lds_char*)smem_w0;
+  lds_char* const W1 = (lds_char*)smem_w1;
+  lds_char* const X0 = (lds_char*)smem_x0;
+  lds_char* const X1 = (lds_char*)smem_x1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -81,36 +105,39 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
       (void*)(static_cast<const uint16_t*>(a.w) + (int64_t)n0 * a.ld_w), (short)0,
       (int)(min(kBN, a.N - n0) * row_w), kRsrcWord3);
 
-  // Thread tid loads chunk c = tid % 8 of tile rows tid / 8 + 64 i.
-  const int lr = tid >> 3, lc = tid & 7;
-  uint32_t vo_x[kLoads], vo_w[kLoads];
+  // Tile loads go straight into LDS (buffer loads with the LDS as
+  // destination): load i of wave w fills tile rows 8 (4 w + i) .. +7, lane l
+  // writing physical chunk l % 8 of row + l / 8, so it fetches the logical
+  // chunk that belongs there.
+  uint32_t vo_x[kLoads], vo_w[kLoads], lch[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    vo_x[i] = (lr + 64 * i) * row_x + lc * 16;
-    vo_w[i] = (lr + 64 * i) * row_w + lc * 16;
+    const int r = 8 * (4 * wave + i) + (lane >> 3);
+    lch[i] = chunk_phys(r, lane & 7);
+    vo_x[i] = r * row_x + lch[i] * 16;
+    vo_w[i] = r * row_w + lch[i] * 16;
   }
-  const int st_off = lr * kRowBytes + (chunk_phys(lr, lc) << 4);  // + 64 i rows
-  u32x4 xreg[kLoads], wreg[kLoads];
-  auto load = [&](int kt) {
+  auto dma = [&](int kt, lds_char* __restrict__ xd, lds_char* __restrict__ wd) {
     const uint32_t so = (uint32_t)kt * kRowBytes;
-    const uint32_t oor = (kt * kBK + lc * 8 >= a.K) ? kOutOfRange : 0u;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      xreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo_x[i] + oor, so, 0);
-      wreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo_w[i] + oor, so, 0);
+      const uint32_t oor = (kt * kBK + (int)lch[i] * 8 >= a.K) ? kOutOfRange : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xd + (4 * wave + i) * 1024), 16,
+                                               vo_x[i] + oor, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wd + (4 * wave + i) * 1024), 16,
+                                               vo_w[i] + oor, so, 0, 0);
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      *reinterpret_cast<u32x4*>(Xs + buf * kTileBytes + st_off + i * 64 * kRowBytes) = xreg[i];
-      *reinterpret_cast<u32x4*>(Ws + buf * kTileBytes + st_off + i * 64 * kRowBytes) = wreg[i];
-    }
+  auto barrier = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // Fragment read offsets: lane reads row (base + r32), logical chunk
   // 2 kk + hf of k-step kk; the 32-row sub-tiles are immediate offsets.
   const int sw = (r32 >> 1) & 7;
+  const int nK = (a.K + kBK - 1) / kBK;
   const int xa = (wm * 128 + r32) * kRowBytes;
   const int wa = (wn * 64 + r32) * kRowBytes;
   int ch[4];
@@ -125,16 +152,9 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nK = (a.K + kBK - 1) / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nK; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nK) load(kt + 1);
-    const char* wb = Ws + buf * kTileBytes + wa;
-    const char* xb = Xs + buf * kTileBytes + xa;
+  auto mma = [&](const lds_char* __restrict__ xc, const lds_char* __restrict__ wc) {
+    const lds_char* wb = wc + wa;
+    const lds_char* xb = xc + xa;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 wf[2], xf[4];
@@ -148,8 +168,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nK) store(buf ^ 1);
-    __syncthreads();
+  };
+  dma(0, X0, W0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  barrier();
+
+  for (int kt = 0; kt < nK; kt += 2) {
+    k_step(kt, kt + 1 < nK, X0, W0, X1, W1, dma, mma);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's tile loads have landed
+    barrier();
+    if (kt + 1 < nK) {
+      k_step(kt + 1, kt + 2 < nK, X1, W1, X0, W0, dma, mma);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      barrier();
+    }
   }
 
   // Epilogue: acc[i][j][4 g + e] is y[m][n + e] for token m = tile row
