@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--chunk-frames", type=int, default=0,
                    help="also time chunk-causal self-attention with chunks of this many "
                         "latent frames (stderr only)")
+    p.add_argument("--no-back-to-back", action="store_true",
+                   help="skip the back-to-back timing of the memory-bound calls (profiler runs "
+                        "that count one launch per call and step)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one device copy of this many MiB (a kernel of known "
                         "traffic, to scale HBM byte counters)")
@@ -413,7 +416,7 @@ def main():
     # previous kernel; the memory-bound calls are also timed in steady state,
     # 20 back-to-back launches between two events.
     for n, fn in zip(names, calls):
-        if n not in bytes_per:
+        if n not in bytes_per or args.no_back_to_back:
             continue
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
