@@ -36,10 +36,10 @@
 //    softmax phase (which reads no LDS) and awaited at its end: group 1
 //    loads the next K tile, group 0 the next V tile, so neither group's
 //    phase carries all the load issue. Rows past k_len fall outside the
-//    buffer resource and read as zero. Each
-//    16-byte chunk of a row is XOR-swizzled so the MFMA operand reads are
-//    bank-conflict free; a load writes 16 bytes per lane at base + 16 lane,
-//    so each lane fetches the global chunk that belongs there.
+//    buffer resource and read as zero. Each 16-byte chunk of a row is
+//    XOR-swizzled so the MFMA operand reads are bank-conflict free; a load
+//    writes 16 bytes per lane at base + 16 lane, so each lane fetches the
+//    global chunk that belongs there.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
 #include "wan_device.h"
@@ -81,8 +81,8 @@ constexpr int kWaitLoads = 0x0F70;
 
 // Barrier between phases, without a memory fence. The only LDS writes inside
 // the main loop are the buffer loads into LDS; the waves that issue them wait
-// for them (kWaitLoads) before the barrier that publishes them. Every LDS read of
-// a phase feeds an MFMA issued before that phase's barrier, so it has
+// for them (kWaitLoads) before the barrier that publishes them. Every LDS
+// read of a phase feeds an MFMA issued before that phase's barrier, so it has
 // completed. The empty asm statements keep the compiler from moving memory
 // accesses across the barrier.
 __device__ __forceinline__ void phase_barrier() {
