@@ -125,300 +125,310 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
   const int nQ = (a.Lq + kBM - 1) / kBM;
   const uint32_t total = (uint32_t)a.B * a.H * nQ;
-  const uint32_t logical = xcd_remap(blockIdx.x, total);
-  const int qt = logical % nQ;
-  const int bh = logical / nQ;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  // Cross-attention workgroups are persistent (the grid has at most 256 of
+  // them, one per CU): with only a few key tiles per query tile, launching a
+  // workgroup per tile costs a noticeable share of its short life. The other
+  // kinds run one item per workgroup.
+  for (uint32_t item = blockIdx.x;;) {
+    const uint32_t logical = xcd_remap(item, total);
+    const int qt = logical % nQ;
+    const int bh = logical / nQ;
+    const int h = bh % a.H;
+    const int b = bh / a.H;
 
-  int kv_len = a.Lk;
-  if (a.k_lens) kv_len = min(max(a.k_lens[b], 0), a.Lk);
-  // Chunk-causal: query row r (global position q_offset + r) sees keys below
-  // min(kv_len, (chunk(q_offset + r) + 1) * chunk_len). The workgroup streams
-  // the tiles its last row needs and masks per row beyond its first row's limit.
-  constexpr bool kCausal = kKind == 2;
-  auto key_limit = [&](int row) {
-    if (!kCausal) return kv_len;
-    const int64_t c = ((int64_t)a.q_offset + row) / a.chunk_len + 1;
-    return (int)min((int64_t)kv_len, c * a.chunk_len);
-  };
-  const int lim_lo = key_limit(min(qt * kBM, a.Lq - 1));
-  const int lim_hi = key_limit(min(qt * kBM + kBM - 1, a.Lq - 1));
-  const int nT = (lim_hi + kBN - 1) / kBN;
+    int kv_len = a.Lk;
+    if (a.k_lens) kv_len = min(max(a.k_lens[b], 0), a.Lk);
+    // Chunk-causal: query row r (global position q_offset + r) sees keys below
+    // min(kv_len, (chunk(q_offset + r) + 1) * chunk_len). The workgroup streams
+    // the tiles its last row needs and masks per row beyond its first row's limit.
+    constexpr bool kCausal = kKind == 2;
+    auto key_limit = [&](int row) {
+      if (!kCausal) return kv_len;
+      const int64_t c = ((int64_t)a.q_offset + row) / a.chunk_len + 1;
+      return (int)min((int64_t)kv_len, c * a.chunk_len);
+    };
+    const int lim_lo = key_limit(min(qt * kBM, a.Lq - 1));
+    const int lim_hi = key_limit(min(qt * kBM + kBM - 1, a.Lq - 1));
+    const int nT = (lim_hi + kBN - 1) / kBN;
 
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.Lq * a.ld_q + h * kHD;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)b * a.Lk * a.ld_k + h * kHD;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (int64_t)b * a.Lk * a.ld_v + h * kHD;
-  const uint32_t row_k = (uint32_t)a.ld_k * 2, row_v = (uint32_t)a.ld_v * 2;
-  // Bytes of valid keys behind each base: anything past them reads as 0.
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)(kv_len * row_k), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.Lq * a.ld_q + h * kHD;
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)b * a.Lk * a.ld_k + h * kHD;
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (int64_t)b * a.Lk * a.ld_v + h * kHD;
+    const uint32_t row_k = (uint32_t)a.ld_k * 2, row_v = (uint32_t)a.ld_v * 2;
+    // Bytes of valid keys behind each base: anything past them reads as 0.
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)(kv_len * row_k), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)(kv_len * row_v), kRsrcWord3);
 
-  // The four waves of a group move a K or V tile from global memory straight
-  // into LDS (buffer loads with the LDS as destination). Load i of wave w
-  // (w = wave % 4) fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
-  // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so it fetches the
-  // logical chunk (l % 16) ^ swizzle of that row.
-  uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int r = ((wave & 3) * kLoadsPerWave + i) * 4 + (lane >> 4);
-    const int p = lane & 15;
-    vo_k[i] = r * row_k + (k_phys(r, p) << 4);  // k_phys is an involution
-    vo_v[i] = r * row_v + (v_phys(r, p) << 4);
-  }
-  auto dma_k = [&](int t, int slot) {
-    const uint32_t sk = (uint32_t)t * kBN * row_k;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (lds_void*)(Ks + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
-          vo_k[i], sk, 0, 0);
-  };
-  auto dma_v = [&](int t, int slot) {
-    const uint32_t sv = (uint32_t)t * kBN * row_v;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (lds_void*)(Vs + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
-          vo_v[i], sv, 0, 0);
-  };
-  // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
-  const int qrow = qt * kBM + wave * 32 + r32;
-  const int lim_row = key_limit(min(qrow, a.Lq - 1));
-  bf16x8 qf[8];
-  {
-    const uint16_t* qr = qg + (int64_t)min(qrow, a.Lq - 1) * a.ld_q + 8 * hf;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-  }
-
-  if (nT > 0 && group == 0) dma_k(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);   // Q and K tile 0 have landed
-  __syncthreads();
-
-  // LDS read addresses (byte offsets inside a tile; the slot, the 32-key
-  // block and the key chunk are immediate offsets).
-  int ka[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) ka[c] = r32 * kRowBytes + (k_phys(r32, 2 * c + hf) << 4);
-  const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
-  int va[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    va[db] = (4 * (g16 >> 1) + e4) * kRowBytes +
-             ((4 * (db ^ e4) + 2 * (g16 & 1) + (q4 >> 1)) << 4) + 8 * (q4 & 1);
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
-  float m_used = -INFINITY;
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
-  f32x16 s[kKB];
-  bf16x8 pf[kKC];
-
-  // GEMM phase of tile jj: O^T += V^T P^T for tile jj - 1 (V slot 1 - KS),
-  // then S^T = K Q^T for tile jj (K slot KS).
-  auto gemm = [&](auto ksc, int jj) {
-    constexpr int KS = decltype(ksc)::value;
-    if (jj >= 1 && jj <= nT) {
-      const char* Vt = Vs + (1 - KS) * kTileBytes;
-      s16x4 lo[4 * kKC], hi[4 * kKC];
-#pragma unroll
-      for (int kc = 0; kc < kKC; ++kc) {
-        const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          lo[kc * 4 + db] = lds_read_tr(Vt + va[db] + krow * kRowBytes);
-          hi[kc * 4 + db] = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
-        }
-      }
-#pragma unroll
-      for (int kc = 0; kc < kKC; ++kc) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const s16x8 cat =
-              __builtin_shufflevector(lo[kc * 4 + db], hi[kc * 4 + db], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, cat), pf[kc], oacc[db], 0, 0, 0);
-        }
-      }
-      // issue order: kAheadV fragments, then one MFMA per fragment read
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadV * 2, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * kKC - kAheadV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadV, 0);
+    // The four waves of a group move a K or V tile from global memory straight
+    // into LDS (buffer loads with the LDS as destination). Load i of wave w
+    // (w = wave % 4) fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
+    // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so it fetches the
+    // logical chunk (l % 16) ^ swizzle of that row.
+    uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
+  #pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int r = ((wave & 3) * kLoadsPerWave + i) * 4 + (lane >> 4);
+      const int p = lane & 15;
+      vo_k[i] = r * row_k + (k_phys(r, p) << 4);  // k_phys is an involution
+      vo_v[i] = r * row_v + (v_phys(r, p) << 4);
     }
-    if (jj < nT) {
-      const char* Kt = Ks + KS * kTileBytes;
-      bf16x8 kf[8 * kKB];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
+    auto dma_k = [&](int t, int slot) {
+      const uint32_t sk = (uint32_t)t * kBN * row_k;
+  #pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (lds_void*)(Ks + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
+            vo_k[i], sk, 0, 0);
+    };
+    auto dma_v = [&](int t, int slot) {
+      const uint32_t sv = (uint32_t)t * kBN * row_v;
+  #pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (lds_void*)(Vs + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
+            vo_v[i], sv, 0, 0);
+    };
+    // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
+    const int qrow = qt * kBM + wave * 32 + r32;
+    const int lim_row = key_limit(min(qrow, a.Lq - 1));
+    bf16x8 qf[8];
+    {
+      const uint16_t* qr = qg + (int64_t)min(qrow, a.Lq - 1) * a.ld_q + 8 * hf;
+  #pragma unroll
+      for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+    }
+
+    if (nT > 0 && group == 0) dma_k(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // Q and K tile 0 have landed
+    __syncthreads();
+
+    // LDS read addresses (byte offsets inside a tile; the slot, the 32-key
+    // block and the key chunk are immediate offsets).
+    int ka[8];
+  #pragma unroll
+    for (int c = 0; c < 8; ++c) ka[c] = r32 * kRowBytes + (k_phys(r32, 2 * c + hf) << 4);
+    const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
+    int va[4];
+  #pragma unroll
+    for (int db = 0; db < 4; ++db)
+      va[db] = (4 * (g16 >> 1) + e4) * kRowBytes +
+               ((4 * (db ^ e4) + 2 * (g16 & 1) + (q4 >> 1)) << 4) + 8 * (q4 & 1);
+
+    f32x16 oacc[4];
+  #pragma unroll
+    for (int d = 0; d < 4; ++d)
+  #pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
+    float m_used = -INFINITY;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x16 s[kKB];
+    bf16x8 pf[kKC];
+
+    // GEMM phase of tile jj: O^T += V^T P^T for tile jj - 1 (V slot 1 - KS),
+    // then S^T = K Q^T for tile jj (K slot KS).
+    auto gemm = [&](auto ksc, int jj) {
+      constexpr int KS = decltype(ksc)::value;
+      if (jj >= 1 && jj <= nT) {
+        const char* Vt = Vs + (1 - KS) * kTileBytes;
+        s16x4 lo[4 * kKC], hi[4 * kKC];
+  #pragma unroll
+        for (int kc = 0; kc < kKC; ++kc) {
+          const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
+  #pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            lo[kc * 4 + db] = lds_read_tr(Vt + va[db] + krow * kRowBytes);
+            hi[kc * 4 + db] = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
+          }
+        }
+  #pragma unroll
+        for (int kc = 0; kc < kKC; ++kc) {
+  #pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const s16x8 cat =
+                __builtin_shufflevector(lo[kc * 4 + db], hi[kc * 4 + db], 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, cat), pf[kc], oacc[db], 0, 0, 0);
+          }
+        }
+        // issue order: kAheadV fragments, then one MFMA per fragment read
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadV * 2, 0);
+  #pragma unroll
+        for (int i = 0; i < 4 * kKC - kAheadV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadV, 0);
+      }
+      if (jj < nT) {
+        const char* Kt = Ks + KS * kTileBytes;
+        bf16x8 kf[8 * kKB];
+  #pragma unroll
+        for (int c = 0; c < 8; ++c)
+  #pragma unroll
+          for (int kb = 0; kb < kKB; ++kb)
+            kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
+  #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
-          kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * kKB + kb], qf[c], s[kb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadK, 0);
-#pragma unroll
-      for (int i = 0; i < 8 * kKB - kAheadK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadK, 0);
-    }
-  };
-
-  // Softmax phase of tile jj: running max/sum update and P = exp2(...) as bf16.
-  auto softmax = [&](int jj) {
-    if (jj < 0 || jj >= nT) return;
-    if ((jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (key >= lim_row) s[kb][v] = -INFINITY;
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+  #pragma unroll
+          for (int kb = 0; kb < kKB; ++kb)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * kKB + kb], qf[c], s[kb], 0, 0, 0);
         }
-    }
-    // P = 2^(s c - m) and its per-lane partial sums
-    float sg[4];
-    auto exps = [&]() __attribute__((always_inline)) {
-      const float neg_m = -m_used;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sg[i] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < kKC; ++kc) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
-          sg[e & 3] += p[e];
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadK, 0);
+  #pragma unroll
+        for (int i = 0; i < 8 * kKB - kAheadK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         }
-        f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
-        pf[kc] = __builtin_convertvector(pv, bf16x8);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadK, 0);
       }
     };
-    bool exact = __any(m_used == -INFINITY);
-    if (!exact) {
-      exps();
-      const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));
-      exact = __any(!(big <= kSumLimit));
-    }
-    if (exact) {
-      float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-      for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
-#pragma unroll
-      for (int kb = 1; kb < kKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float mt = mx * a.scale_log2;
-      if (__any(mt > m_used + kRescaleThreshold)) {
-        const float mn = fmaxf(m_used, mt);
-        // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
-        const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ls[i] *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
-        m_used = mn;
-      }
-      exps();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ls[i] += sg[i];
-  };
 
-  // Two groups of waves run the same phase sequence, group 1 one interval
-  // behind group 0, so that in every interval one wave of each SIMD is in a
-  // GEMM phase (MFMA) while the other is in a softmax phase (VALU):
-  //   phase 2j: GEMM(j) = PV(j-1) + S(j);   phase 2j+1: softmax(j).
-  // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
-  // slots of K(j-1) and V(j-2) are free from interval 2j on (their last
-  // reader, group 1's GEMM(j-1), ran in interval 2j-1). Group 1 loads K(j+1)
-  // during its softmax phase of interval 2j, group 0 loads V(j) during its
-  // softmax phase of interval 2j+1; each waits for its loads at the end of
-  // that phase, before the barrier that publishes them, and both are in
-  // place for group 0's GEMM(j+1) in interval 2j+2.
-  const int nIntervals = 2 * nT + 2;
-  for (int i = 0; i < nIntervals; i += 4) {
-    const int j0 = i >> 1;
-    if (group == 0) gemm(Int<0>{}, j0);
-    else {
-      if (j0 + 1 < nT) dma_k(j0 + 1, 1);
-      softmax(j0 - 1);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    }
-    phase_barrier();
-    if (group == 0) {
-      if (j0 < nT) dma_v(j0, 0);
-      softmax(j0);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    } else gemm(Int<0>{}, j0);
-    phase_barrier();
-    const int j1 = j0 + 1;
-    if (group == 0) gemm(Int<1>{}, j1);
-    else {
-      if (j1 + 1 < nT) dma_k(j1 + 1, 0);
-      softmax(j0);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    }
-    phase_barrier();
-    if (group == 0) {
-      if (j1 < nT) dma_v(j1, 1);
-      softmax(j1);
-      __builtin_amdgcn_s_waitcnt(kWaitLoads);
-    } else gemm(Int<1>{}, j1);
-    phase_barrier();
-  }
-
-  // ---- epilogue: combine the two half-waves' partial sums, normalise, store.
-  float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
-                                                     false, false);
-    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  if (qrow < a.Lq) {
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        f32x4 x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
-                   oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 y = __builtin_convertvector(x, bf16x4);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hf) = __builtin_bit_cast(u32x2, y);
+    // Softmax phase of tile jj: running max/sum update and P = exp2(...) as bf16.
+    auto softmax = [&](int jj) {
+      if (jj < 0 || jj >= nT) return;
+      if ((jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
+  #pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+            if (key >= lim_row) s[kb][v] = -INFINITY;
+          }
       }
-    if (a.lse && hf == 0) {
-      a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
-          lsum > 0.f ? m_used * 0.6931471805599453f + logf(lsum) : -INFINITY;
+      // P = 2^(s c - m) and its per-lane partial sums
+      float sg[4];
+      auto exps = [&]() __attribute__((always_inline)) {
+        const float neg_m = -m_used;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) sg[i] = 0.f;
+  #pragma unroll
+        for (int kc = 0; kc < kKC; ++kc) {
+          float p[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
+            sg[e & 3] += p[e];
+          }
+          f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
+          pf[kc] = __builtin_convertvector(pv, bf16x8);
+        }
+      };
+      bool exact = __any(m_used == -INFINITY);
+      if (!exact) {
+        exps();
+        const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));
+        exact = __any(!(big <= kSumLimit));
+      }
+      if (exact) {
+        float mx = fmaxf(s[0][0], s[0][1]);
+  #pragma unroll
+        for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
+  #pragma unroll
+        for (int kb = 1; kb < kKB; ++kb)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mt = mx * a.scale_log2;
+        if (__any(mt > m_used + kRescaleThreshold)) {
+          const float mn = fmaxf(m_used, mt);
+          // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
+          const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) ls[i] *= alpha;
+  #pragma unroll
+          for (int d = 0; d < 4; ++d)
+  #pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+          m_used = mn;
+        }
+        exps();
+      }
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) ls[i] += sg[i];
+    };
+
+    // Two groups of waves run the same phase sequence, group 1 one interval
+    // behind group 0, so that in every interval one wave of each SIMD is in a
+    // GEMM phase (MFMA) while the other is in a softmax phase (VALU):
+    //   phase 2j: GEMM(j) = PV(j-1) + S(j);   phase 2j+1: softmax(j).
+    // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
+    // slots of K(j-1) and V(j-2) are free from interval 2j on (their last
+    // reader, group 1's GEMM(j-1), ran in interval 2j-1). Group 1 loads K(j+1)
+    // during its softmax phase of interval 2j, group 0 loads V(j) during its
+    // softmax phase of interval 2j+1; each waits for its loads at the end of
+    // that phase, before the barrier that publishes them, and both are in
+    // place for group 0's GEMM(j+1) in interval 2j+2.
+    const int nIntervals = 2 * nT + 2;
+    for (int i = 0; i < nIntervals; i += 4) {
+      const int j0 = i >> 1;
+      if (group == 0) gemm(Int<0>{}, j0);
+      else {
+        if (j0 + 1 < nT) dma_k(j0 + 1, 1);
+        softmax(j0 - 1);
+        __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      }
+      phase_barrier();
+      if (group == 0) {
+        if (j0 < nT) dma_v(j0, 0);
+        softmax(j0);
+        __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      } else gemm(Int<0>{}, j0);
+      phase_barrier();
+      const int j1 = j0 + 1;
+      if (group == 0) gemm(Int<1>{}, j1);
+      else {
+        if (j1 + 1 < nT) dma_k(j1 + 1, 0);
+        softmax(j0);
+        __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      }
+      phase_barrier();
+      if (group == 0) {
+        if (j1 < nT) dma_v(j1, 1);
+        softmax(j1);
+        __builtin_amdgcn_s_waitcnt(kWaitLoads);
+      } else gemm(Int<1>{}, j1);
+      phase_barrier();
     }
+
+    // ---- epilogue: combine the two half-waves' partial sums, normalise, store.
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                       false, false);
+      lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (qrow < a.Lq) {
+      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+      uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
+  #pragma unroll
+      for (int db = 0; db < 4; ++db)
+  #pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          f32x4 x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
+                     oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 y = __builtin_convertvector(x, bf16x4);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hf) = __builtin_bit_cast(u32x2, y);
+        }
+      if (a.lse && hf == 0) {
+        a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
+            lsum > 0.f ? m_used * 0.6931471805599453f + logf(lsum) : -INFINITY;
+      }
+    }
+    if (kKind != 1) break;
+    item += gridDim.x;
+    if (item >= total) break;
+    __syncthreads();   // the next item reuses the LDS slots
   }
 }
 
@@ -430,7 +440,10 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s) {
   const dim3 grid((unsigned)total), block(kThreads);
   switch (kind) {
     case 0: hipLaunchKernelGGL(attn_fwd_kernel<0>, grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL(attn_fwd_kernel<1>, grid, block, 0, s, a); break;
+    case 1:
+      hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3((unsigned)(total < 256 ? total : 256)), block, 0,
+                         s, a);
+      break;
     case 2: hipLaunchKernelGGL(attn_fwd_kernel<2>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
