@@ -214,6 +214,23 @@ def test_adaln_per_token_modulation_and_inplace():
     compare("per-token h", synth.bf16_bits(ho), h)
 
 
+def test_cross_attn_many_tiles_mixed_lengths():
+    """More query tiles than the 256 persistent cross-attention workgroups
+    (2 x 8 heads x 20 tiles = 320), so workgroups loop over several tiles;
+    sample 0 has no text keys (zero output), sample 1 a ragged 300."""
+    _announce("cross_attn 320 query tiles, context lens 0/300")
+    B, Lq, Lk, H = 2, 20 * 256, 512, 8
+    C = 128 * H
+    q, k, v = _rand((B, Lq, C), 41), _rand((B, Lk, C), 42), _rand((B, Lk, C), 43)
+    cl = torch.tensor([0, 300], dtype=torch.int32)
+    o = ops.cross_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, context_lens=cl.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0)
+    ref, _ = O.cross_attention(synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v), H,
+                               cl.numpy())
+    compare("cross 320 tiles", synth.bf16_bits(o), ref)
+
+
 @pytest.mark.parametrize("pattern", ["rising", "falling", "spike", "sawtooth"])
 def test_self_attn_running_max_paths(pattern):
     """Logits whose tile maxima follow a set pattern across the 12 key tiles
