@@ -60,7 +60,8 @@ constexpr int kHD = 128;                     // head size
 constexpr int kRowBytes = kHD * 2;
 constexpr int kTileBytes = kBN * kRowBytes;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLoadsPerWave = kTileBytes / 1024 / (kWaves / 2);  // per tile and wave of a group, 1 KiB each
+// 1 KiB tile loads per tile and wave of the loading group
+constexpr int kLoadsPerWave = kTileBytes / 1024 / (kWaves / 2);
 constexpr float kRescaleThreshold = 8.0f;    // log2 units
 constexpr float kSumLimit = 256.0f;          // per-lane tile sum of P that forces the tile max
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
@@ -163,11 +164,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
     // The four waves of a group move a K or V tile from global memory straight
     // into LDS (buffer loads with the LDS as destination). Load i of wave w
-    // (w = wave % 4) fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l writes physical
-    // chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so it fetches the
-    // logical chunk (l % 16) ^ swizzle of that row.
+    // (w = wave % 4) fills tile rows 4(kLoadsPerWave w + i) .. +3: lane l
+    // writes physical chunk l % 16 of row 4(kLoadsPerWave w + i) + l / 16, so
+    // it fetches the logical chunk (l % 16) ^ swizzle of that row.
     uint32_t vo_k[kLoadsPerWave], vo_v[kLoadsPerWave];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int r = ((wave & 3) * kLoadsPerWave + i) * 4 + (lane >> 4);
       const int p = lane & 15;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     auto dma_k = [&](int t, int slot) {
       const uint32_t sk = (uint32_t)t * kBN * row_k;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (lds_void*)(Ks + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     };
     auto dma_v = [&](int t, int slot) {
       const uint32_t sv = (uint32_t)t * kBN * row_v;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (lds_void*)(Vs + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     bf16x8 qf[8];
     {
       const uint16_t* qr = qg + (int64_t)min(qrow, a.Lq - 1) * a.ld_q + 8 * hf;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
     }
 
@@ -207,19 +208,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     // LDS read addresses (byte offsets inside a tile; the slot, the 32-key
     // block and the key chunk are immediate offsets).
     int ka[8];
-  #pragma unroll
+#pragma unroll
     for (int c = 0; c < 8; ++c) ka[c] = r32 * kRowBytes + (k_phys(r32, 2 * c + hf) << 4);
     const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
     int va[4];
-  #pragma unroll
+#pragma unroll
     for (int db = 0; db < 4; ++db)
       va[db] = (4 * (g16 >> 1) + e4) * kRowBytes +
                ((4 * (db ^ e4) + 2 * (g16 & 1) + (q4 >> 1)) << 4) + 8 * (q4 & 1);
 
     f32x16 oacc[4];
-  #pragma unroll
+#pragma unroll
     for (int d = 0; d < 4; ++d)
-  #pragma unroll
+#pragma unroll
       for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
     float m_used = -INFINITY;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -233,18 +234,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       if (jj >= 1 && jj <= nT) {
         const char* Vt = Vs + (1 - KS) * kTileBytes;
         s16x4 lo[4 * kKC], hi[4 * kKC];
-  #pragma unroll
+#pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
           const int krow = 32 * (kc >> 1) + 16 * (kc & 1);
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < 4; ++db) {
             lo[kc * 4 + db] = lds_read_tr(Vt + va[db] + krow * kRowBytes);
             hi[kc * 4 + db] = lds_read_tr(Vt + va[db] + (krow + 8) * kRowBytes);
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < 4; ++db) {
             const s16x8 cat =
                 __builtin_shufflevector(lo[kc * 4 + db], hi[kc * 4 + db], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         }
         // issue order: kAheadV fragments, then one MFMA per fragment read
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadV * 2, 0);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4 * kKC - kAheadV; ++i) {
           __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
@@ -264,23 +265,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       if (jj < nT) {
         const char* Kt = Ks + KS * kTileBytes;
         bf16x8 kf[8 * kKB];
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; ++c)
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < kKB; ++kb)
             kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; ++c) {
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < kKB; ++kb)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * kKB + kb], qf[c], s[kb], 0, 0, 0);
+            s[kb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c * kKB + kb], qf[c], s[kb], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAheadK, 0);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8 * kKB - kAheadK; ++i) {
           __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
@@ -293,9 +295,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     auto softmax = [&](int jj) {
       if (jj < 0 || jj >= nT) return;
       if ((jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
             if (key >= lim_row) s[kb][v] = -INFINITY;
@@ -305,12 +307,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       float sg[4];
       auto exps = [&]() __attribute__((always_inline)) {
         const float neg_m = -m_used;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) sg[i] = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
           float p[8];
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) {
             p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
             sg[e & 3] += p[e];
@@ -327,11 +329,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       }
       if (exact) {
         float mx = fmaxf(s[0][0], s[0][1]);
-  #pragma unroll
+#pragma unroll
         for (int v = 2; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
-  #pragma unroll
+#pragma unroll
         for (int kb = 1; kb < kKB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
@@ -343,17 +345,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
           const float mn = fmaxf(m_used, mt);
           // a row with no visible key yet keeps m = -inf (and alpha 1, not NaN)
           const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) ls[i] *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int d = 0; d < 4; ++d)
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
           m_used = mn;
         }
         exps();
       }
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 4; ++i) ls[i] += sg[i];
     };
 
@@ -410,15 +412,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     if (qrow < a.Lq) {
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
       uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
-  #pragma unroll
+#pragma unroll
       for (int db = 0; db < 4; ++db)
-  #pragma unroll
+#pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           f32x4 x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
                      oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 y = __builtin_convertvector(x, bf16x4);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hf) = __builtin_bit_cast(u32x2, y);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hf) =
+              __builtin_bit_cast(u32x2, y);
         }
       if (a.lse && hf == 0) {
         a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
