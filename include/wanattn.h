@@ -132,7 +132,9 @@ wanStatus_t wan_qk_norm_rope3d(void* q_out, void* k_out, const void* q,
  *          the host: values are clamped to [0, L].
  * softmax_scale  > 0, or <= 0 for 1/sqrt(D).
  * Errors: WAN_ERROR_INVALID_VALUE (NULL/misaligned pointers, bad sizes or
- * strides, o overlapping an input), WAN_ERROR_NOT_SUPPORTED (D != 128).
+ * strides, o overlapping an input), WAN_ERROR_NOT_SUPPORTED (D != 128, or the
+ * keys of one (batch, head) spanning more than 4 GiB: L * max(ld_k, ld_v) * 2
+ * bytes, since they are addressed with 32-bit byte offsets).
  */
 wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q,
                               const void* k, const void* v,
