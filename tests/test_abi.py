@@ -115,6 +115,10 @@ def test_self_attn_rejections(L):
     assert attn(L, scale=float("inf")) == INV
     assert attn(L, B=0) == OK
     assert attn(L, Lt=0) == OK
+    # keys of one (batch, head) spanning more than 4 GiB (32-bit byte offsets)
+    far = dict(o=A, q=A + (1 << 36), k=A + (2 << 36), v=A + (3 << 36), lq=4096, lk=4096,
+               lv=4096, lo=4096)
+    assert attn(L, Lt=1 << 20, **far) == NS
 
 
 def test_cross_attn_rejections(L):
