@@ -36,39 +36,55 @@ def _rand(shape, seed, std=1.0):
     return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
 
 
-def _check_quantised(qz, q, k, v, H):
+def _heads(bits, H, hs):
+    """Channels of heads ``hs`` of a [B, L, H*d] array, as [B, L, len(hs)*d]."""
+    B, L, C = bits.shape
+    return np.ascontiguousarray(bits.reshape(B, L, H, C // H)[:, :, hs].reshape(B, L, -1))
+
+
+def _check_quantised(qz, q, k, v, H, hs=None):
+    """Codes and scales of heads ``hs`` (all if None) bit for bit against the
+    oracle's quantisers on those heads' channels (every block is per (batch,
+    head), so a head's codes do not depend on the other heads)."""
     B, L = qz["B"], qz["L"]
     nT = (L + 63) // 64
+    hs = list(range(H)) if hs is None else list(hs)
+    sel = torch.tensor(hs, device=qz["q8"].device)
     for name, x in (("q8", q), ("k8", k)):
-        codes, sc = O.quantize_int8_blocks(synth.bf16_bits(x), H)
-        got = qz[name].cpu().numpy().reshape(B, H, nT * 64, -1)
+        codes, sc = O.quantize_int8_blocks(_heads(synth.bf16_bits(x), H, hs), len(hs))
+        got = qz[name].index_select(1, sel).cpu().numpy().reshape(B, len(hs), nT * 64, -1)
         assert np.array_equal(got[:, :, :L], codes), name
         assert not got[:, :, L:].any(), name + " padding"
-        gs = qz["q_scale" if name == "q8" else "k_scale"].cpu().numpy()
+        gs = qz["q_scale" if name == "q8" else "k_scale"].index_select(1, sel).cpu().numpy()
         assert np.array_equal(gs, sc), name + " scales"
-    codes, ex, _ = O.quantize_v_mxfp8(synth.bf16_bits(v), H)
-    got = qz["v8"].cpu().numpy().transpose(0, 1, 2, 4, 3).reshape(B, H, nT * 64, -1)
+    codes, ex, vdeq = O.quantize_v_mxfp8(_heads(synth.bf16_bits(v), H, hs), len(hs))
+    got = qz["v8"].index_select(1, sel).cpu().numpy()
+    got = got.transpose(0, 1, 2, 4, 3).reshape(B, len(hs), nT * 64, -1)
     assert np.array_equal(got[:, :, :L], codes), "v8"
-    sv = qz["v_scale"].cpu().numpy()            # [B, H, nT, 2, 32, D/32]
+    sv = qz["v_scale"].index_select(1, sel).cpu().numpy()    # [B, h, nT, 2, 32, D/32]
     D = sv.shape[-1] * 32
-    byt = sv.transpose(0, 1, 2, 3, 5, 4).reshape(B, H, nT * 2, D)
+    byt = sv.transpose(0, 1, 2, 3, 5, 4).reshape(B, len(hs), nT * 2, D)
     nb = ex.shape[2]
     assert np.array_equal(byt[:, :, :nb].astype(np.int64), ex + 127), "v scales"
+    return float(np.abs(vdeq).max(initial=0.0))
 
 
-def _run(name, q, k, v, H, k_lens=None, scale=0.0, rows=None):
-    print(f"[case] attn8 {name}: {tuple(q.shape)} H={H} k_lens={k_lens}", flush=True)
+def _run(name, q, k, v, H, k_lens=None, scale=0.0, rows=None, hs=None):
+    """Quantise and attend on the GPU over all heads; check heads ``hs`` (all
+    if None) and query rows ``rows`` (all if None) against the oracle."""
+    print(f"[case] attn8 {name}: {tuple(q.shape)} H={H} k_lens={k_lens} heads={hs}", flush=True)
     qz = ops.quantize_qkv_8bit(q.to(DEV), k.to(DEV), v.to(DEV), H)
     kl = None if k_lens is None else torch.tensor(k_lens, dtype=torch.int32, device=DEV)
     o, lse = ops.self_attn_fwd_8bit(qz, k_lens=kl, scale=scale, return_lse=True)
     torch.cuda.synchronize()
-    _check_quantised(qz, q, k, v, H)
+    vmax = _check_quantised(qz, q, k, v, H, hs)
     sel = slice(None) if rows is None else torch.as_tensor(rows)
-    ref, rl = O.attention_8bit(synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v), H,
-                               k_lens=k_lens, scale=scale or None, rows=rows)
-    vmax = float(np.abs(O.quantize_v_mxfp8(synth.bf16_bits(v), H)[2]).max())
-    compare_8bit(f"attn8 {name}", synth.bf16_bits(o[:, sel]), ref, vmax)
-    gl = lse[:, :, sel].cpu().numpy().astype(np.float64)
+    hsel = list(range(H)) if hs is None else list(hs)
+    ref, rl = O.attention_8bit(*(_heads(synth.bf16_bits(x), H, hsel) for x in (q, k, v)),
+                               len(hsel), k_lens=k_lens, scale=scale or None, rows=rows)
+    got = o[:, sel].view(o.shape[0], -1, H, o.shape[2] // H)[:, :, hsel].flatten(2)
+    compare_8bit(f"attn8 {name}", synth.bf16_bits(got), ref, vmax)
+    gl = lse[:, hsel][:, :, sel].cpu().numpy().astype(np.float64)
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(gl), fin)
     assert np.max(np.abs(gl[fin] - rl[fin]), initial=0.0) < 1e-3
@@ -115,3 +131,15 @@ def test_attn8_wan_480p_and_bf16_agreement():
     ref = o16.float().pow(2).mean().sqrt().item()
     print(f"[attn8] 480p relative RMS difference from the bf16 kernel: {d / ref:.4f}", flush=True)
     assert d < 0.06 * ref
+
+
+@pytest.mark.timeout(900)
+def test_attn8_a14b_720p_cfg_sampled_heads():
+    """The shape the benchmark times the 8-bit call on: 2 x 75,600 tokens
+    (21 x 45 x 80 grid, both CFG halves), 40 heads, one launch of each call.
+    Codes and scales of heads 0, 13, 26 and 39 are checked bit for bit on
+    every token; the output and lse on the sampled rows of those heads in
+    both batch entries."""
+    w = BY_NAME["a14b-720p-cfg"]
+    q, k, v = (synth.tensor(w, t, "cpu") for t in ("q", "k", "v"))
+    _run("a14b-720p-cfg", q, k, v, w.heads, rows=synth.sample_rows(w), hs=[0, 13, 26, 39])

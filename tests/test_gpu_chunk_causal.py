@@ -36,19 +36,29 @@ def _rand(shape, seed, std=1.0):
     return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
 
 
-def _check(name, q, k, v, H, q_offset, chunk_len, k_lens=None, rows=None, scale=0.0):
+def _heads(bits, H, hs):
+    """Channels of heads ``hs`` of a [B, L, H*d] array, as [B, L, len(hs)*d]."""
+    B, L, C = bits.shape
+    return np.ascontiguousarray(bits.reshape(B, L, H, C // H)[:, :, hs].reshape(B, L, -1))
+
+
+def _check(name, q, k, v, H, q_offset, chunk_len, k_lens=None, rows=None, scale=0.0, hs=None):
+    """One launch over all heads; heads ``hs`` (all if None) and query rows
+    ``rows`` (all if None) compared with the oracle."""
     print(f"[case] chunk-causal {name}: q {tuple(q.shape)} k {tuple(k.shape)} "
-          f"offset {q_offset} chunk {chunk_len}", flush=True)
+          f"offset {q_offset} chunk {chunk_len} heads {hs}", flush=True)
     kl_dev = None if k_lens is None else torch.tensor(k_lens, dtype=torch.int32, device=DEV)
     o, lse = ops.chunk_causal_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, q_offset, chunk_len,
                                        k_lens=kl_dev, scale=scale, return_lse=True)
     torch.cuda.synchronize()
     sel = slice(None) if rows is None else torch.as_tensor(rows)
-    ref, rl = O.chunk_causal_attention(synth.bf16_bits(q), synth.bf16_bits(k),
-                                       synth.bf16_bits(v), H, q_offset, chunk_len,
-                                       k_lens=k_lens, scale=scale or None, rows=rows)
-    compare(name, synth.bf16_bits(o[:, sel]), ref)
-    got_l = lse[:, :, sel].cpu().numpy().astype(np.float64)
+    hsel = list(range(H)) if hs is None else list(hs)
+    ref, rl = O.chunk_causal_attention(*(_heads(synth.bf16_bits(x), H, hsel) for x in (q, k, v)),
+                                       len(hsel), q_offset, chunk_len, k_lens=k_lens,
+                                       scale=scale or None, rows=rows)
+    got = o[:, sel].view(o.shape[0], -1, H, o.shape[2] // H)[:, :, hsel].flatten(2)
+    compare(name, synth.bf16_bits(got), ref)
+    got_l = lse[:, hsel][:, :, sel].cpu().numpy().astype(np.float64)
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(got_l), fin), f"{name}: -inf lse pattern differs"
     assert np.max(np.abs(got_l[fin] - rl[fin]), initial=0.0) < 1e-3, name
@@ -122,3 +132,18 @@ def test_wan_480p_three_frame_chunks(form):
         q = q[:, off:].contiguous()
         rows = np.unique(np.concatenate([rows % chunk, [0, chunk - 1]]))
         _check("480p newest chunk", q, k, v, w.heads, off, chunk, rows=rows)
+
+
+@pytest.mark.timeout(900)
+def test_a14b_720p_cfg_three_frame_chunks():
+    """The launch the benchmark times: the whole 21 x 45 x 80 clip (2 x 75,600
+    tokens, 40 heads) in chunks of 3 latent frames (10,800 tokens). Sampled
+    rows of heads 0, 21 and 39 in both batch entries, plus the first and last
+    row of every chunk."""
+    w = BY_NAME["a14b-720p-cfg"]
+    chunk = 3 * 45 * 80
+    q, k, v = (synth.tensor(w, t, "cpu") for t in ("q", "k", "v"))
+    starts = np.arange(0, w.tokens, chunk)
+    rows = np.unique(np.concatenate([synth.sample_rows(w), starts,
+                                     np.minimum(starts + chunk, w.tokens) - 1]))
+    _check("a14b-720p-cfg 3-frame chunks", q, k, v, w.heads, 0, chunk, rows=rows, hs=[0, 21, 39])
