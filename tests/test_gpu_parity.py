@@ -172,6 +172,43 @@ def test_attn_empty_keys_and_peaked_logits():
     compare("peaked", synth.bf16_bits(o2), ref2)
 
 
+@pytest.mark.parametrize("kind", ["self", "cross", "chunk-causal"])
+def test_keys_past_length_take_no_part(kind):
+    """Key and value rows at or past a batch entry's key length hold +inf and
+    NaN: they must not reach the output (o would turn NaN if a value row past
+    the length entered the P V product, even with P = 0). Lengths 70 and 131
+    end inside a 64-key tile and are not tile multiples; the oracle gets the
+    same tensors with those rows zeroed, which by definition changes nothing."""
+    _announce(f"{kind}: keys past the length hold inf / NaN")
+    B, H, Lq = 2, 2, 200
+    C = 128 * H
+    Lk = 300 if kind == "cross" else Lq
+    q = _rand((B, Lq, C), 71)
+    k, v = _rand((B, Lk, C), 72), _rand((B, Lk, C), 73)
+    lens = [70, 131]
+    kz, vz = k.clone(), v.clone()
+    for b, n in enumerate(lens):
+        k[b, n:] = float("inf")
+        v[b, n:] = float("nan")
+        kz[b, n:] = 0
+        vz[b, n:] = 0
+    kl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    qb, kb, vb = (synth.bf16_bits(t) for t in (q, kz, vz))
+    if kind == "self":
+        o = ops.self_attn_fwd(qd, kd, vd, H, k_lens=kl)
+        ref, _ = O.self_attention(qb, kb, vb, H, lens)
+    elif kind == "cross":
+        o = ops.cross_attn_fwd(qd, kd, vd, H, context_lens=kl)
+        ref, _ = O.cross_attention(qb, kb, vb, H, lens)
+    else:
+        o = ops.chunk_causal_attn_fwd(qd, kd, vd, H, 0, 64, k_lens=kl)
+        ref, _ = O.chunk_causal_attention(qb, kb, vb, H, 0, 64, k_lens=lens)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any(), f"{kind}: a key row past the length reached the output"
+    compare(f"{kind} keys past length", synth.bf16_bits(o), ref)
+
+
 @pytest.mark.parametrize("flags", ["norm+rope", "norm", "rope", "per_head_norm+rope"])
 def test_norm_rope_flags_and_fused_buffer(flags):
     _announce(f"norm_rope flags={flags}")
