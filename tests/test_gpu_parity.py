@@ -233,6 +233,54 @@ def test_norm_rope_flags_and_fused_buffer(flags):
     assert np.array_equal(out[..., 2 * C:], ref_in[..., 2 * C:])   # v untouched
 
 
+@pytest.mark.parametrize("H", [44, 61, 64])
+def test_widest_rows(H):
+    """Rows of 5632, 7808 and 8192 channels (up to the 8192-channel limit of
+    the row kernels; 7808 ends inside a 512-channel chunk): q/k RMSNorm over
+    the whole row and per head with RoPE, and the AdaLN call with and
+    without a gated residual."""
+    _announce(f"widest rows: H={H} C={128 * H}")
+    B, grid = 2, (3, 4, 5)
+    L, C = 60, 128 * H
+    q, k = _rand((B, L, C), 91, std=2.0), _rand((B, L, C), 92)
+    g = torch.Generator().manual_seed(9)
+    gq, gk = (1 + 0.1 * torch.randn(C, generator=g)).float(), (1 + 0.1 * torch.randn(C, generator=g)).float()
+    for per_head in (False, True):
+        qo, ko = ops.qk_norm_rope3d(q.to(DEV), k.to(DEV), H, grid, gq.to(DEV), gk.to(DEV),
+                                    per_head=per_head)
+        torch.cuda.synchronize()
+        for name, x, gn, out in (("q", q, gq, qo), ("k", k, gk, ko)):
+            ref = O.qk_norm_rope3d(synth.bf16_bits(x), gn.numpy(), grid, H, per_head=per_head)
+            compare(f"C={C} per_head={per_head} {name}", synth.bf16_bits(out), ref)
+    x, y = _rand((B, L, C), 93), _rand((B, L, C), 94)
+    e = (torch.randn(B, 6, C, generator=g) * 0.3).float()
+    en = e.numpy().astype(np.float64)
+    xb, yb = synth.bf16_bits(x), synth.bf16_bits(y)
+    ed = e.to(DEV)
+    xo, ho = ops.adaln_modulate_gate(x.to(DEV), y.to(DEV), ed[:, 2], ed[:, 0], ed[:, 1])
+    _, h1 = ops.adaln_modulate_gate(x.to(DEV), None, None, ed[:, 3], ed[:, 4], want_x=False)
+    torch.cuda.synchronize()
+    r, h = O.adaln_modulate_gate(xb, yb, en[:, 2], en[:, 0], en[:, 1], 1e-6)
+    compare(f"C={C} adaln x'", synth.bf16_bits(xo), r)
+    compare(f"C={C} adaln h", synth.bf16_bits(ho), h)
+    _, h1r = O.adaln_modulate_gate(xb, None, None, en[:, 3], en[:, 4], 1e-6)
+    compare(f"C={C} adaln h (no residual)", synth.bf16_bits(h1), h1r)
+
+
+@pytest.mark.parametrize("grid", [(1024, 1, 3), (2, 1024, 1), (1, 3, 1024)])
+def test_rope_grid_at_table_limit(grid):
+    """Grid axes of 1024 positions, the length of the per-axis frequency
+    table the RoPE call supports."""
+    _announce(f"rope grid {grid}")
+    B, H = 1, 2
+    L, C = grid[0] * grid[1] * grid[2], 128 * H
+    q = _rand((B, L, C), 95)
+    qo, _ = ops.qk_norm_rope3d(q.to(DEV), None, H, grid, norm=False)
+    torch.cuda.synchronize()
+    ref = O.qk_norm_rope3d(synth.bf16_bits(q), None, grid, H, norm=False)
+    compare(f"rope grid {grid}", synth.bf16_bits(qo), ref)
+
+
 def test_adaln_per_token_modulation_and_inplace():
     _announce("adaln per-token + in place")
     B, L, C = 2, 33, 1536
