@@ -4,7 +4,9 @@ Usage: python -m attention_wan_qk_amd.build  (or build() from Python)
 
 Every .hip source and the C ABI layer are compiled to objects under
 ``_build/`` at the repository root, in parallel, and linked into
-``attention_wan_qk_amd/libwanattn.so``. Always recompiles.
+``attention_wan_qk_amd/libwanattn.so``. The measurement aids in
+``csrc/probe/`` (include/wanpeak.h) are linked into a library of their own,
+``attention_wan_qk_amd/libwanpeak.so``. Always recompiles.
 """
 
 from __future__ import annotations
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwanattn.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libwanpeak.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -57,19 +61,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        probe = ex.submit(_compile, PROBE_SRC)
+        objs = list(ex.map(_compile, srcs))
+        probe_obj = probe.result()
+    _link(LIB, objs)
+    _link(PROBE_LIB, [probe_obj])
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB}")
     return LIB
 
 

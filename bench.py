@@ -10,7 +10,9 @@ outputs are synthetic tensors of the same shape.
 
 Prints one JSON line (rank 0). `value` is the self-attention FLOP of a step
 (4 L^2 d H B) divided by the whole step's time; the roofline object reports
-the self-attention kernel alone, timed with events on its stream.
+the self-attention kernel alone, timed with events on its stream, against
+the spec peak and against the rate of a plain MFMA loop measured in the same
+run after the timed steps (libwanpeak.so; --no-measured-peaks skips it).
 """
 
 from __future__ import annotations
@@ -55,6 +57,9 @@ def parse():
     p.add_argument("--no-back-to-back", action="store_true",
                    help="skip the back-to-back timing of the memory-bound calls (profiler runs "
                         "that count one launch per call and step)")
+    p.add_argument("--no-measured-peaks", action="store_true",
+                   help="skip the sustained-MFMA loop and device copy (libwanpeak) run after "
+                        "the timed steps")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one device copy of this many MiB (a kernel of known "
                         "traffic, to scale HBM byte counters)")
@@ -297,6 +302,52 @@ def breakdown_causal(args, w, ops, q, k, v, o, full_ms):
         "time_vs_full": round(ms / full_ms, 4)}}), file=sys.stderr, flush=True)
 
 
+def measured_peaks(memory_gbs):
+    """Sustained rates of two plain loops (libwanpeak.so), run after the timed
+    steps: a bf16 MFMA loop (512 workgroups of 4 waves, 4 independent
+    accumulator chains per wave, random operands, ~0.3 s per launch, so that
+    the chip reaches the clock it holds under full MFMA load; fastest of 3
+    launches) and a 2 GiB nontemporal device copy (fastest of 10 launches).
+    Returns (MFMA TFLOP/s, copy GB/s); the memory calls' rates are printed
+    against the copy on stderr."""
+    import torch
+    from attention_wan_qk_amd import peaks
+    dev = "cuda:0"
+    g = torch.Generator(device="cpu")
+    g.manual_seed(20250)
+    operands = torch.randn(2 * peaks.THREADS * 8, generator=g).to(torch.bfloat16).to(dev)
+    blocks, iters = 512, 2_000_000
+    out = torch.empty(blocks * peaks.THREADS, dtype=torch.float32, device=dev)
+    peaks.mfma_bf16_loop(operands, out, blocks, 20_000)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(3):
+        peaks.mfma_bf16_loop(operands, out, blocks, iters)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    mfma_tf = peaks.mfma_loop_flop(blocks, iters) / (min(ms) * 1e-3) / 1e12
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    peaks.copy(dst, src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    ev[0].record()
+    for i in range(10):
+        peaks.copy(dst, src)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n / (min(ev[i].elapsed_time(ev[i + 1]) for i in range(10)) * 1e-3) / 1e9
+    del src, dst
+    print(json.dumps({"measured_peaks": {
+        "mfma_bf16_loop_tflops": round(mfma_tf, 1), "mfma_loop_ms": [round(m, 2) for m in ms],
+        "mfma_loop_frac_of_spec": round(mfma_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "copy_gbs": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+        "memory_calls_frac_of_copy": {k: round(v / copy_gbs, 4) for k, v in memory_gbs.items()},
+    }}), file=sys.stderr, flush=True)
+    return mfma_tf, copy_gbs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,6 +521,11 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_measured_peaks:
+        gbs = {n: r.get("back_to_back_gbs", r["gbs"]) for n, r in breakdown.items() if "gbs" in r}
+        mfma_tf, _ = measured_peaks(gbs)
+        result["roofline"]["measured_peak"] = round(mfma_tf, 1)
+        result["roofline"]["frac_of_measured_peak"] = round(attn_tflops / mfma_tf, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, (t["q"], t["k"], t["v"]), args.cpu_seconds)
     print(json.dumps(result), flush=True)

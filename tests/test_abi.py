@@ -235,3 +235,42 @@ def test_8bit_rejections(L):
     assert at(lo=100) == INV
     assert at(scale=float("nan")) == INV
     assert at(v8=None) == INV
+
+
+PEAK_HEADER = os.path.join(ROOT, "include", "wanpeak.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    from attention_wan_qk_amd import peaks
+    if not os.path.exists(peaks.LIB_PATH):
+        from attention_wan_qk_amd.build import build
+        build(verbose=False)
+    return peaks.lib()
+
+
+def test_peak_library_exports_and_host_checks(P):
+    """libwanpeak.so (the benchmark's measurement aids) exports what
+    include/wanpeak.h declares and rejects bad arguments before launching."""
+    from attention_wan_qk_amd import peaks
+    declared = sorted(set(re.findall(r"^\s*int\s+(wanpeak_\w+)\s*\(", open(PEAK_HEADER).read(),
+                                     re.M)))
+    assert declared == ["wanpeak_copy", "wanpeak_mfma_bf16_loop"]
+    out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(re.findall(r"\bT (wanpeak_\w+)", out)) == set(declared)
+    loop = P.wanpeak_mfma_bf16_loop
+    assert loop(None, A, 1, 1, None) == 1
+    assert loop(A, None, 1, 1, None) == 1
+    assert loop(A, A, 0, 1, None) == 1
+    assert loop(A, A, 65537, 1, None) == 1
+    assert loop(A, A, 1, 0, None) == 1
+    assert loop(A + 8, A, 1, 1, None) == 1          # operands not 16-byte aligned
+    assert loop(A, A + 2, 1, 1, None) == 1          # out not 4-byte aligned
+    cp = P.wanpeak_copy
+    assert cp(None, A, 16, None) == 1
+    assert cp(A, A + MB, 24, None) == 1              # not a multiple of 16
+    assert cp(A + 8, A + MB, 16, None) == 1          # misaligned
+    assert cp(A, A + 16, 32, None) == 1              # overlapping ranges
+    assert cp(A, A + MB, 0, None) == 0               # nothing to do: no launch
+    assert peaks.mfma_loop_flop(512, 10) == 512 * 4 * 10 * 4 * 32768

@@ -1,0 +1,46 @@
+"""The measurement aids of libwanpeak.so on the GPU: the MFMA loop's FLOP
+accounting (all-ones operands make every accumulator element 16 per MFMA,
+so a thread's sum is 4 chains x 16 elements x 16 x iters) and the copy
+(bytes identical, including a ragged last workgroup)."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+from attention_wan_qk_amd import peaks
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("blocks,iters", [(1, 1), (3, 5), (512, 7)])
+def test_mfma_loop_counts(blocks, iters):
+    print(f"[case] mfma loop blocks={blocks} iters={iters}", flush=True)
+    ops_ = torch.ones(2 * peaks.THREADS * 8, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((blocks * peaks.THREADS,), -1.0, dtype=torch.float32, device=DEV)
+    peaks.mfma_bf16_loop(ops_, out, blocks, iters)
+    torch.cuda.synchronize()
+    assert torch.all(out == 4 * 16 * 16 * iters)
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1024 + 48, (1 << 20) + 48])
+def test_copy(nbytes):
+    print(f"[case] copy {nbytes} bytes", flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8).to(DEV)
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)
+    peaks.copy(dst[:nbytes], src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert not dst[nbytes:].any()
