@@ -378,6 +378,7 @@ wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8, float* q_
   }
   // outputs: codes B*H*nT*64*D bytes each, scales B*H*nT floats / B*H*nT*256 bytes
   const int64_t nT = (L + 63) / 64, tiles = (int64_t)B * H * nT;
+  if (tiles > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;   // one workgroup per block
   const Range outs[6] = {
       {reinterpret_cast<uintptr_t>(q8), reinterpret_cast<uintptr_t>(q8) + (uintptr_t)(tiles * 64 * D)},
       {reinterpret_cast<uintptr_t>(k8), reinterpret_cast<uintptr_t>(k8) + (uintptr_t)(tiles * 64 * D)},
@@ -417,6 +418,7 @@ wanStatus_t wan_self_attn_fwd_8bit(void* o, float* lse, const int8_t* q8, const 
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return WAN_ERROR_INVALID_VALUE;
   const int64_t nT = (L + 63) / 64, tiles = (int64_t)B * H * nT;
   if (nT > 4096) return WAN_ERROR_NOT_SUPPORTED;   // key-block scales held in LDS
+  if ((int64_t)B * H * ((L + 255) / 256) > 0x7fffffff) return WAN_ERROR_NOT_SUPPORTED;
   const Range ro = span_bf16(o, (int64_t)B * L, ld_o, C);
   const Range ins[6] = {
       {reinterpret_cast<uintptr_t>(q8), reinterpret_cast<uintptr_t>(q8) + (uintptr_t)(tiles * 64 * D)},

@@ -296,7 +296,8 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
  * ld_q, ld_k, ld_v; ld = 0 means H*D) into the layouts above. Outputs must
  * not overlap each other or the inputs. Key lengths play no part.
  * Errors: WAN_ERROR_INVALID_VALUE for NULL/misaligned pointers, bad sizes or
- * strides, overlaps; WAN_ERROR_NOT_SUPPORTED for D != 128.
+ * strides, overlaps; WAN_ERROR_NOT_SUPPORTED for D != 128, H*D > 2^24, or
+ * B*H*nT > 2^31 - 1 (one workgroup per block).
  */
 wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
                                   float* q_scale, float* k_scale,
@@ -320,7 +321,8 @@ wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
  * k_lens device int32 [B] or NULL (clamped to [0, L]).
  * softmax_scale  > 0, or <= 0 for 1/sqrt(D).
  * Errors: WAN_ERROR_INVALID_VALUE (NULL/misaligned pointers, bad sizes,
- * overlaps), WAN_ERROR_NOT_SUPPORTED (D != 128, or L > 262144).
+ * overlaps), WAN_ERROR_NOT_SUPPORTED (D != 128, H*D > 2^24, L > 262144, or
+ * more than 2^31 - 1 workgroups: B*H*ceil(L / 256)).
  */
 wanStatus_t wan_self_attn_fwd_8bit(void* o, float* lse, const int8_t* q8,
                                    const int8_t* k8, const uint8_t* v8,

@@ -220,6 +220,7 @@ def test_8bit_rejections(L):
     assert qz(lq=200) == INV                  # row stride < H*D
     assert qz(k8=A + 16) == INV               # outputs overlap
     assert qz(q=A + 2 * MB) == INV            # output overlaps an input
+    assert qz(B=1 << 20, L=1 << 18) == NS     # 2^33 blocks: beyond one launch
 
     def at(**kw):
         a = dict(o=A, lse=None, q8=A + MB, k8=A + 2 * MB, v8=A + 3 * MB, sq=A + 4 * MB,
@@ -235,6 +236,8 @@ def test_8bit_rejections(L):
     assert at(lo=100) == INV
     assert at(scale=float("nan")) == INV
     assert at(v8=None) == INV
+    assert at(L=(1 << 18) + 1) == NS          # key-block scales beyond the LDS table
+    assert at(B=1 << 20, L=1 << 18, H=16) == NS   # 2^34 workgroups: beyond one launch
 
 
 PEAK_HEADER = os.path.join(ROOT, "include", "wanpeak.h")
