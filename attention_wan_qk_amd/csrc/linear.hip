@@ -14,10 +14,10 @@
 //    accumulator tiles of 32 x 32 per wave, two waves per SIMD).
 //  * K advances in steps of 64 through a double-buffered LDS stage (x and W
 //    tiles, 32 KiB each). The tiles of step k+1 are moved by buffer loads
-//    whose destination is the LDS (no register staging), issued before the
-//    MFMAs of step k into the other buffer; each wave waits for its own
-//    loads before the step's barrier, which publishes them: one barrier per
-//    step. The two buffers are reached through restrict pointers of an
+//    whose destination is the LDS (no register staging), issued with the
+//    MFMAs of the first two of step k's four 16-deep k-steps into the other
+//    buffer; each wave waits for its own loads before the step's barrier,
+//    which publishes them: one barrier per step. The two buffers are reached through restrict pointers of an
 //    inlined step function, so the compiler can tell that the loads in
 //    flight do not write what the step's LDS reads read, and places no wait
 //    before those reads.
@@ -44,6 +44,7 @@ constexpr int kThreads = 512;
 constexpr int kRowBytes = kBK * 2;       // 128
 constexpr int kTileBytes = kBM * kRowBytes;  // 32 KiB (x and W tiles are the same size)
 constexpr int kLoads = kTileBytes / 16 / kThreads;  // 1 KiB loads per wave per tile: 4
+constexpr int kLoadGroups = 2;          // the next stage's loads go out with the first 2 k-steps
 constexpr int kGroupM = 4;               // token tiles per band
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -66,8 +67,12 @@ template <typename Dma, typename Mma>
 __device__ __forceinline__ void k_step(int kt, bool more, const lds_char* __restrict__ xc,
                                        const lds_char* __restrict__ wc, lds_char* __restrict__ xn,
                                        lds_char* __restrict__ wn, Dma& dma, Mma& mma) {
-  if (more) dma(kt + 1, xn, wn);
-  mma(xc, wc);
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    if (more && kk < kLoadGroups) dma(kt + 1, xn, wn, kk);
+    mma(xc, wc, kk);
+    __builtin_amdgcn_sched_barrier(0);   // keep each group of loads with its k-step
+  }
 }
 
 }  // namespace
@@ -117,10 +122,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
     vo_x[i] = r * row_x + lch[i] * 16;
     vo_w[i] = r * row_w + lch[i] * 16;
   }
-  auto dma = [&](int kt, lds_char* __restrict__ xd, lds_char* __restrict__ wd) {
+  // group g < kLoadGroups issues loads i with i / (kLoads / kLoadGroups) == g;
+  // group -1 issues all of them.
+  auto dma = [&](int kt, lds_char* __restrict__ xd, lds_char* __restrict__ wd, int group) {
     const uint32_t so = (uint32_t)kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+      if (group >= 0 && i / (kLoads / kLoadGroups) != group) continue;
       const uint32_t oor = (kt * kBK + (int)lch[i] * 8 >= a.K) ? kOutOfRange : 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xd + (4 * wave + i) * 1024), 16,
                                                vo_x[i] + oor, so, 0, 0);
@@ -152,11 +160,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto mma = [&](const lds_char* __restrict__ xc, const lds_char* __restrict__ wc) {
+  // MFMAs of k-step kk (16 of the stage's 64 K values).
+  auto mma = [&](const lds_char* __restrict__ xc, const lds_char* __restrict__ wc, int kk) {
     const lds_char* wb = wc + wa;
     const lds_char* xb = xc + xa;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    {
       bf16x8 wf[2], xf[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) wf[i] = lds_read16(wb + ch[kk] + i * 32 * kRowBytes);
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
     }
   };
-  dma(0, X0, W0);
+  dma(0, X0, W0, -1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   barrier();
 
