@@ -37,7 +37,8 @@ def _rand(shape, seed, std=1.0, dtype=torch.bfloat16):
 
 @pytest.mark.parametrize("M,N,K,bias", [(1, 8, 8, False), (7, 24, 72, True), (300, 264, 200, True),
                                         (257, 512, 128, False), (513, 1536, 1536, True),
-                                        (1024, 768, 4096, True), (64, 5120, 40, True)])
+                                        (1024, 768, 4096, True), (64, 5120, 40, True),
+                                        (100, 264, 136, True), (65, 392, 192, False)])
 def test_linear_shapes(M, N, K, bias):
     print(f"[case] linear M={M} N={N} K={K} bias={bias}", flush=True)
     x = _rand((M, K), 71)
