@@ -385,3 +385,30 @@ def test_determinism_and_side_stream():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.timeout(600)
+def test_keys_spanning_more_than_2gib():
+    """One head over 2^23 + 1000 keys: each of K and V spans 2.15 GB, past the
+    2^31-byte mark of the kernels' 32-bit in-buffer offsets (the calls accept
+    up to 4 GiB). Cross-attention over all keys, and the chunk-causal call in
+    its key-cache form with a key length that ends inside the last tile;
+    sampled query rows against the oracle."""
+    Lk, Lq, C = (1 << 23) + 1000, 256, 128
+    _announce(f"keys spanning {Lk * C * 2 / 1e9:.3f} GB (Lk={Lk}, one head)")
+    q = _rand((1, Lq, C), 81)
+    k, v = _rand((1, Lk, C), 82), _rand((1, Lk, C), 83)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_x = ops.cross_attn_fwd(qd, kd, vd, 1)
+    kl = Lk - 500
+    o_c = ops.chunk_causal_attn_fwd(qd, kd, vd, 1, Lk - Lq, 1 << 30,
+                                    k_lens=torch.tensor([kl], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    rows = np.array([0, 1, 31, 32, 127, 128, 200, 255])
+    qb, kb, vb = synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v)
+    ref, _ = O.cross_attention(qb, kb, vb, 1, rows=rows)
+    compare("cross over 2^23 keys", synth.bf16_bits(o_x[:, torch.as_tensor(rows)]), ref)
+    ref, _ = O.chunk_causal_attention(qb, kb, vb, 1, Lk - Lq, 1 << 30, k_lens=[kl], rows=rows)
+    compare("key cache over 2^23 keys, k_len cut", synth.bf16_bits(o_c[:, torch.as_tensor(rows)]),
+            ref)
