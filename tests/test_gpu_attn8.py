@@ -143,3 +143,14 @@ def test_attn8_a14b_720p_cfg_sampled_heads():
     w = BY_NAME["a14b-720p-cfg"]
     q, k, v = (synth.tensor(w, t, "cpu") for t in ("q", "k", "v"))
     _run("a14b-720p-cfg", q, k, v, w.heads, rows=synth.sample_rows(w), hs=[0, 13, 26, 39])
+
+
+@pytest.mark.timeout(600)
+def test_attn8_longest_sequence():
+    """L = 262144 (4096 key blocks), the most the 8-bit call accepts: its
+    per-block key scales fill the LDS table exactly. One head; all codes and
+    scales, and sampled rows including block and tile edges."""
+    L, H = 1 << 18, 1
+    q, k, v = (_rand((1, L, 128 * H), s) for s in (91, 92, 93))
+    rows = np.array([0, 1, 63, 64, 255, 256, 131071, 131072, L - 257, L - 256, L - 65, L - 1])
+    _run("L=262144", q, k, v, H, rows=rows)
