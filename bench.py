@@ -496,7 +496,9 @@ def main():
 
     traffic = measured_traffic("attn_fwd_kernel", w.name)
     result = {
-        "metric": "self-attn TFLOP/s (4*L^2*d*H*B) at A14B 720P CFG (75600 tok), whole block step",
+        "metric": ("self-attn TFLOP/s (4*L^2*d*H*B) at A14B 720P CFG (75600 tok), whole block step"
+                   if w.name == "a14b-720p-cfg" else
+                   f"self-attn TFLOP/s (4*L^2*d*H*B) at {w.name} ({w.tokens} tok), whole block step"),
         "value": round(attn_flop / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

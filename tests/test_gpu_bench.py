@@ -41,7 +41,7 @@ def test_bench_json_line_on_the_tiny_workload():
         assert key in rec, key
     assert rec["n_gpus"] == 1 and rec["steps"] == 2 and rec["warmup"] == 1
     assert rec["value"] > 0 and rec["ms_per_step"] > 0
-    assert rec["config"]["workload"] == "tiny-5x8x8"
+    assert rec["config"]["workload"] == "tiny-5x8x8" and "tiny-5x8x8" in rec["metric"]
     roof = rec["roofline"]
     assert roof["bound"] == "mfma" and roof["peak"] == 2500.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
