@@ -399,19 +399,36 @@ def linear(x, w, bias=None) -> np.ndarray:
 # 8-bit attention (the pages' inference speed path)
 # ----------------------------------------------------------------------------
 # "论文专题讲解：Wan2.1", inference-optimisation table, row "8-bit
-# FlashAttention": S = Q K^T in INT8, O = P V in FP8, accumulation across
-# key blocks in FP32. Readings (the table gives no more): Q and K are
-# quantised per (batch, head, block of 64 tokens) to symmetric INT8 with an
-# fp32 scale amax / 127; V is quantised to FP8 E4M3 per (batch, head,
-# channel, block of 32 keys) with a power-of-two (E8M0) scale, the OCP
-# microscaling recipe; P is rounded to FP8 E4M3 after the row maximum (an
-# integer in log2 units) is subtracted, and the softmax denominator sums the
-# rounded P (so the weights applied to v sum to one). Every quantised code is decided in fp32, as the kernel decides
-# it (numpy float32 arithmetic is IEEE-correctly rounded, like the GPU's).
+# FlashAttention": the scores S = Q K^T are formed from INT8 operands, the
+# output O = P V from FP8 operands, and the accumulation across key blocks is
+# kept in FP32. That row fixes the formats and nothing else; the readings
+# taken (each one on format grounds):
+#  * q and k: symmetric INT8 (codes -127..127, one scale per block) over
+#    blocks of 64 tokens of one (batch, head); scale = amax / 127 stored as
+#    fp32; code = round-half-even of x * (127 / amax), that product formed in
+#    fp32 (a quantised code is an integer decided by floating point, so the
+#    decision is pinned to one precision).
+#  * v: FP8 E4M3 with the OCP microscaling recipe: one power-of-two (E8M0)
+#    scale per 32 keys of one channel, 2^(floor(log2 amax) - 8) (8 = the
+#    exponent of E4M3's largest binade), elements clamped to +-448 and
+#    rounded to nearest even.
+#  * Keys at or past k_len are padding: they take no part in attention, so
+#    they are also left out of k's and v's block scales and get code 0.
+#  * The score of a (query, key) pair is the exact integer dot product of the
+#    codes times both block scales and the softmax scale.
+#  * P, the FP8 operand of P V, is E4M3 of 2^(t - m): t = the score in log2
+#    units, m = ceil(max_j t) - 7 an integer. A power-of-two offset leaves the
+#    E4M3 rounding of every normal value that of the weight itself, and this
+#    one puts the row maximum in (2^6, 2^7], inside E4M3's normal range
+#    [2^-6, 448] with room above it.
+#  * The softmax denominator is not an operand of the FP8 product: it sums
+#    the unrounded weights 2^(t - m), accumulated in high precision beside
+#    the product (float64 here).
+# Every step after the quantisation is carried out in float64.
 INT8_BLOCK = 64
 MX_BLOCK = 32
 E4M3_MAX = 448.0
-LOG2E = 1.4426950408889634
+P_OFFSET = 7    # m = ceil(max t) - P_OFFSET
 
 
 def e4m3_bits_to_f64(bits) -> np.ndarray:
@@ -446,18 +463,30 @@ def f64_to_e4m3_bits(x) -> np.ndarray:
     return (sign | code).astype(np.uint8)
 
 
-def quantize_int8_blocks(x, H: int, block: int = INT8_BLOCK):
+def _valid_rows(B: int, L: int, lens):
+    """[B, L] bool: token l of sample b is valid (l < lens[b]; all if lens is None)."""
+    if lens is None:
+        return np.ones((B, L), dtype=bool)
+    n = np.clip(np.asarray(lens, dtype=np.int64).reshape(B), 0, L)
+    return np.arange(L)[None, :] < n[:, None]
+
+
+def quantize_int8_blocks(x, H: int, block: int = INT8_BLOCK, lens=None):
     """Symmetric INT8 per (batch, head, block of ``block`` tokens).
 
-    x: [B, L, H*d]. Returns codes int8 [B, H, L, d] and scales float32
-    [B, H, ceil(L / block)]: amax = max |x| over the block (all L tokens, key
-    lengths play no part), code = round_half_even(x * (127 / amax)) in fp32,
-    clamped to +-127, scale = amax / 127 in fp32 (amax = 0: codes 0, scale 0).
+    x: [B, L, H*d]; lens: per-sample valid token count or None (all valid).
+    Returns codes int8 [B, H, L, d] and scales float32 [B, H, ceil(L / block)]:
+    amax = max |x| over the valid rows of the block, code =
+    round_half_even(fp32(x * fp32(127 / amax))) clamped to +-127, scale =
+    fp32(amax / 127); rows past the valid count and blocks with amax = 0 get
+    code 0 (and scale 0 when the whole block is zero).
     """
     x = _f64(x)
     B, L, C = x.shape
     d = C // H
     nb = -(-L // block)
+    valid = _valid_rows(B, L, lens)
+    x = np.where(valid[:, :, None], x, 0.0)
     xh = x.reshape(B, L, H, d).transpose(0, 2, 1, 3).astype(np.float32)   # exact (bf16 -> f32)
     codes = np.zeros((B, H, L, d), dtype=np.int8)
     scales = np.zeros((B, H, nb), dtype=np.float32)
@@ -473,19 +502,21 @@ def quantize_int8_blocks(x, H: int, block: int = INT8_BLOCK):
     return codes, scales
 
 
-def quantize_v_mxfp8(v, H: int, block: int = MX_BLOCK):
+def quantize_v_mxfp8(v, H: int, block: int = MX_BLOCK, lens=None):
     """FP8 E4M3 per (batch, head, channel, block of ``block`` keys) with a
     power-of-two scale (OCP microscaling): X = 2^(floor(log2 amax) - 8), the
     largest E4M3 binade being 2^8; element = E4M3(clamp(v / X, +-448)).
 
-    v: [B, L, H*d]. Returns codes uint8 [B, H, L, d], the scale exponents
-    int [B, H, ceil(L / block), d] (X = 2^exp; amax = 0 gives exp -127 and
-    zero codes) and the dequantised values float64 [B, H, L, d].
+    v: [B, L, H*d]; lens as in quantize_int8_blocks (rows past it are zero).
+    Returns codes uint8 [B, H, L, d], the scale exponents int
+    [B, H, ceil(L / block), d] (X = 2^exp; amax = 0 gives exp -127 and zero
+    codes) and the dequantised values float64 [B, H, L, d].
     """
     v = _f64(v)
     B, L, C = v.shape
     d = C // H
     nb = -(-L // block)
+    v = np.where(_valid_rows(B, L, lens)[:, :, None], v, 0.0)
     vh = v.reshape(B, L, H, d).transpose(0, 2, 1, 3)
     codes = np.zeros((B, H, L, d), dtype=np.uint8)
     exps = np.full((B, H, nb, d), -127, dtype=np.int64)
@@ -504,58 +535,54 @@ def quantize_v_mxfp8(v, H: int, block: int = MX_BLOCK):
     return codes, exps, deq
 
 
-def _f32_fma(a, b, c) -> np.ndarray:
-    """fp32 fused multiply-add: the product of two fp32 values is exact in
-    float64, the sum is rounded once more to fp32."""
-    return (np.asarray(a, np.float64) * np.asarray(b, np.float64)
-            + np.asarray(c, np.float64)).astype(np.float32)
+def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None, on_head=None):
+    """8-bit self-attention as read from the "8-bit FlashAttention" row (see
+    the section comment): INT8 scores, FP8 probabilities and values, the rest
+    in float64.
 
-
-def attention_8bit(q, k, v, H: int, k_lens=None, scale=None, rows=None):
-    """8-bit self-attention: INT8 scores, FP8 probabilities and values, fp32
-    accumulation (see the section comment for the readings).
-
-    q, k, v: [B, L, H*d]. Per (b, h) and query row i, with n = k_len:
-      S_ij   = sum_d qc_id kc_jd                    (exact integer dot product)
-      mult   = fp32(fp32(sq_blk(i) sk_blk(j)) c),   c = fp32(scale) * fp32(log2 e) in fp32
-                                                    (scale defaults to 1 / sqrt(d) in fp32),
-               floored at 1e-30 and truncated to 22 significant bits (the reading
-               that lets the INT8 accumulator be read as fp32 without a conversion)
-      m_i    = ceil(max_j S_ij mult) - 7            (integer, log2 units)
-      t_ij   = fp32 fma(S_ij, mult, -m_i);  p_ij = fp32(2^t_ij);  P_ij = E4M3(p_ij)
-      o_i    = sum_j P_ij vdeq_j / sum_j P_ij,   lse_i = ln 2 (m_i + log2 sum_j P_ij)
-    Returns o [B, rows, H*d] and lse [B, H, rows]; n = 0 gives o = 0,
-    lse = -inf. The integer offset m_i only moves P by a power of two, which
-    leaves every normal E4M3 rounding unchanged.
+    q, k, v: [B, L, H*d]. Per (b, h) and query row i, with n = k_len[b]:
+      S_ij = sum_e qc_ie kc_je                   (exact integer dot product)
+      s_ij = S_ij * sq_i * sk_j * scale          (scale defaults to 1/sqrt(d))
+      t_ij = s_ij * log2(e),  m_i = ceil(max_{j<n} t_ij) - 7
+      p_ij = 2^(t_ij - m_i),  P_ij = E4M3(p_ij)  (round to nearest even)
+      l_i  = sum_{j<n} p_ij
+      o_i  = sum_{j<n} P_ij vdeq_j / l_i
+      lse_i = ln 2 * (m_i + log2 l_i)            (= log sum_j exp(s_ij))
+    Returns o [B, rows, H*d] and lse [B, H, rows]; n = 0 gives o = 0 and
+    lse = -inf. ``on_head(b, h, terms)``, if given, receives each (batch,
+    head)'s float64 terms over the selected rows and the n visible keys, a
+    dict with t, m, p, P, l, the dequantised values v and ``unit`` (t of one
+    unit of S, i.e. sq_i sk_j scale log2 e), for tests that bound what a
+    finite-precision evaluation of these steps may change.
     """
     qc, sq = quantize_int8_blocks(q, H)
-    kc, sk = quantize_int8_blocks(k, H)
-    _, _, vdeq = quantize_v_mxfp8(v, H)
+    kc, sk = quantize_int8_blocks(k, H, lens=k_lens)
+    _, _, vdeq = quantize_v_mxfp8(v, H, lens=k_lens)
     B, _, Lq, d = qc.shape
     Lk = kc.shape[2]
-    sc = (np.float32(scale) if scale is not None and scale > 0
-          else np.float32(1) / np.sqrt(np.float32(d)))
-    c = np.float32(sc * np.float32(LOG2E))
+    sc = float(scale) if scale is not None and scale > 0 else 1.0 / np.sqrt(d)
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((B, rows.size, H * d))
     lse = np.full((B, H, rows.size), -np.inf)
-    kblk = np.arange(Lk) // INT8_BLOCK
     qblk = rows // INT8_BLOCK
+    kblk = np.arange(Lk) // INT8_BLOCK
     for b in range(B):
         n = Lk if k_lens is None else max(0, min(int(k_lens[b]), Lk))
         if n == 0:
             continue
         for h in range(H):
-            # integer dot products, exact in float64 (|S| < 2^22)
             S = qc[b, h, rows].astype(np.float64) @ kc[b, h, :n].astype(np.float64).T
-            sqk = (sq[b, h, qblk][:, None] * sk[b, h, kblk[:n]][None, :]).astype(np.float32)
-            mult = np.maximum((sqk * c).astype(np.float32), np.float32(1e-30))
-            mult = (mult.view(np.uint32) & np.uint32(0xFFFFFFFC)).view(np.float32)
-            m = np.ceil((S * mult.astype(np.float64)).max(axis=1)) - 7
-            t = _f32_fma(S.astype(np.float32), mult, -m[:, None])
-            p = np.exp2(t.astype(np.float64)).astype(np.float32).astype(np.float64)
+            unit = sq[b, h, qblk].astype(np.float64)[:, None] \
+                * sk[b, h, kblk[:n]].astype(np.float64)[None, :] * sc
+            s = S * unit
+            t = s / np.log(2.0)
+            m = np.ceil(t.max(axis=1)) - P_OFFSET
+            p = np.exp2(t - m[:, None])
             P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))
-            l = P.sum(axis=1)
+            l = p.sum(axis=1)
             o[b, :, h * d:(h + 1) * d] = (P @ vdeq[b, h, :n]) / l[:, None]
             lse[b, h] = np.log(2.0) * (m + np.log2(l))
+            if on_head is not None:
+                on_head(b, h, {"t": t, "m": m, "p": p, "P": P, "l": l, "v": vdeq[b, h, :n],
+                               "unit": unit / np.log(2.0)})
     return o, lse

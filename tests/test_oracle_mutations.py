@@ -54,7 +54,18 @@ MUTATIONS = [
     ("fp8 ties away from zero", "    n = np.rint(a / q)                          # ties to even",
      "    n = np.floor(a / q + 0.5)"),
     ("P left unrounded", "            P = e4m3_bits_to_f64(f64_to_e4m3_bits(p))", "            P = p"),
-    ("denominator of unrounded p", "            l = P.sum(axis=1)", "            l = p.sum(axis=1)"),
+    ("denominator of rounded P", "            l = p.sum(axis=1)", "            l = P.sum(axis=1)"),
+    ("P offset not an integer", "m = np.ceil(t.max(axis=1)) - P_OFFSET",
+     "m = t.max(axis=1) - P_OFFSET"),
+    ("P offset one binade low", "P_OFFSET = 7 ", "P_OFFSET = 8 "),
+    ("8-bit score without softmax scale",
+     "* sk[b, h, kblk[:n]].astype(np.float64)[None, :] * sc",
+     "* sk[b, h, kblk[:n]].astype(np.float64)[None, :]"),
+    ("q scale of the wrong block", "    qblk = rows // INT8_BLOCK", "    qblk = 0 * rows"),
+    ("key padding in k scales", "    kc, sk = quantize_int8_blocks(k, H, lens=k_lens)",
+     "    kc, sk = quantize_int8_blocks(k, H)"),
+    ("padding rows kept by the quantisers", "    x = np.where(valid[:, :, None], x, 0.0)",
+     "    x = x"),
 ]
 
 

@@ -572,87 +572,174 @@ def test_mxfp8_value_quantization():
 E4M3_CLAMP = 448.0
 
 
-def _attention_8bit_loops(q, k, v, H, k_len, scale):
-    """The 8-bit algorithm written with scalar loops (tiny inputs only)."""
+def test_quantizers_leave_out_keys_past_length():
+    """Keys at or past k_len are padding: the k and v quantisers form their
+    block scales from the valid rows only and give the padding code 0."""
+    B, L, H, d = 2, 150, 1, 16
+    x = RNG.standard_normal((B, L, H * d))
+    x[0, 100:] *= 1000.0                 # huge padding past k_len = 100 (block 1 is mixed)
+    x[1, 40:] = np.inf                   # non-finite padding past k_len = 40
+    lens = [100, 40]
+    codes, sc = O.quantize_int8_blocks(x, H, lens=lens)
+    vc, ex, vd = O.quantize_v_mxfp8(x, H, lens=lens)
+    for b, n in enumerate(lens):
+        assert not codes[b, 0, n:].any() and not vc[b, 0, n:].any() and not vd[b, 0, n:].any()
+        for j in range(3):
+            valid = x[b, j * 64:min((j + 1) * 64, n), :]
+            amax = np.abs(valid).max() if valid.size else 0.0
+            assert sc[b, 0, j] == (np.float32(np.float32(amax) / np.float32(127)) if amax else 0)
+        for j in range(5):
+            valid = x[b, j * 32:min((j + 1) * 32, n), :]
+            for c in range(d):
+                amax = np.abs(valid[:, c]).max() if valid.size else 0.0
+                want = math.frexp(amax)[1] - 1 - 8 if amax > 0 else -127
+                assert ex[b, 0, j, c] == want
+    # the valid rows' codes are those of the same rows with zero padding
+    z = np.where(np.arange(L)[None, :, None] < np.array(lens)[:, None, None], x, 0.0)
+    cz, sz = O.quantize_int8_blocks(z, H)
+    assert np.array_equal(codes, cz) and np.array_equal(sc, sz)
+    assert np.array_equal(vd, O.quantize_v_mxfp8(z, H)[2])
+
+
+def _dequantised(q, k, v, H, k_lens):
+    """Dequantised operands [B, H, L, d]: code * block scale."""
     qc, sq = O.quantize_int8_blocks(q, H)
-    kc, sk = O.quantize_int8_blocks(k, H)
-    _, _, vd = O.quantize_v_mxfp8(v, H)
-    B, _, L, d = qc.shape
-    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
-    out = np.zeros((B, L, H * d))
-    for b in range(B):
-        for h in range(H):
-            for i in range(L):
-                ts, mults = [], []
-                for j in range(k_len):
-                    s = sum(int(qc[b, h, i, e]) * int(kc[b, h, j, e]) for e in range(d))
-                    mult = max(np.float32(np.float32(sq[b, h, i // 64] * sk[b, h, j // 64]) * c),
-                               np.float32(1e-30))
-                    mult = np.array([mult], np.float32).view(np.uint32) & np.uint32(0xFFFFFFFC)
-                    mult = mult.view(np.float32)[0]
-                    ts.append(s)
-                    mults.append(mult)
-                m = math.ceil(max(s * float(mu) for s, mu in zip(ts, mults))) - 7
-                num = np.zeros(d)
-                den = 0.0
-                for j, (s, mu) in enumerate(zip(ts, mults)):
-                    t = np.float32(float(np.float32(s)) * float(mu) - m)
-                    p = float(np.float32(2.0 ** float(t)))
-                    P = float(O.e4m3_bits_to_f64(O.f64_to_e4m3_bits(p)))
-                    num += P * vd[b, h, j]
-                    den += P
-                out[b, i, h * d:(h + 1) * d] = num / den
-    return out
+    kc, sk = O.quantize_int8_blocks(k, H, lens=k_lens)
+    _, _, vd = O.quantize_v_mxfp8(v, H, lens=k_lens)
+    blk = np.arange(qc.shape[2]) // 64
+    qd = qc.astype(np.float64) * sq[:, :, blk][..., None].astype(np.float64)
+    kd = kc.astype(np.float64) * sk[:, :, blk][..., None].astype(np.float64)
+    return qd, kd, vd
 
 
-def test_attention_8bit_against_loops():
-    B, L, H, d = 1, 70, 2, 16
-    q, k, v = RNG.standard_normal((3, B, L, H * d))
-    o, lse = O.attention_8bit(q, k, v, H, k_lens=[61], scale=0.3)
-    ref = _attention_8bit_loops(q, k, v, H, 61, 0.3)
-    assert np.allclose(o, ref, rtol=0, atol=1e-12)
-
-
-def test_attention_8bit_properties():
+def test_attention_8bit_against_exact_attention_on_dequantised_operands():
+    """Against exact attention (torch SDPA, float64) on the dequantised
+    operands, only the rounding of the weights in the P V product differs:
+    each P_ij is within half an E4M3 spacing of p_ij, i.e. 2^-4 p_ij where p
+    is normal (>= 2^-6) and 2^-10 below, and the denominator is exact. With
+    w = p / l the softmax weights and l >= 2^6 (the row maximum of p lies in
+    (2^6, 2^7]):  |o - o_exact|_d <= 2^-4 sum_j w_j |v_jd| + 2^-16 sum_j |v_jd|.
+    lse is exactly the log-sum-exp of the scores (scipy)."""
     B, L, H, d = 2, 150, 2, 32
     q, k, v = RNG.standard_normal((3, B, L, H * d))
-    o, lse = O.attention_8bit(q, k, v, H)
-    # close to exact attention on the unquantised inputs
-    ex, exl = O.self_attention(q, k, v, H)
-    assert np.sqrt(np.mean((o - ex) ** 2)) < 0.06 * np.sqrt(np.mean(ex ** 2))
-    # against exact attention on the dequantised operands, only P's rounding differs:
-    # each weight moves by at most 2^-4 of itself (normal) or 2^-10 (subnormal), in the
-    # numerator and the denominator alike
-    qc, sq = O.quantize_int8_blocks(q, H)
-    kc, sk = O.quantize_int8_blocks(k, H)
-    _, _, vd = O.quantize_v_mxfp8(v, H)
-    blk = np.arange(L) // 64
+    k_lens = [150, 97]
+    for scale in (None, 0.6):
+        o, lse = O.attention_8bit(q, k, v, H, k_lens=k_lens, scale=scale)
+        qd, kd, vd = _dequantised(q, k, v, H, k_lens)
+        sc = scale or 1 / math.sqrt(d)
+        for b, n in enumerate(k_lens):
+            for h in range(H):
+                Q, K, V = (torch.from_numpy(np.ascontiguousarray(a)) for a in
+                           (qd[b, h], kd[b, h, :n], vd[b, h, :n]))
+                ex = F.scaled_dot_product_attention(Q[None], K[None], V[None], scale=sc)[0].numpy()
+                s = qd[b, h] @ kd[b, h, :n].T * sc
+                w = np.exp(s - s.max(axis=1, keepdims=True))
+                w /= w.sum(axis=1, keepdims=True)
+                av = np.abs(vd[b, h, :n])
+                bound = 2.0 ** -4 * (w @ av) + 2.0 ** -16 * av.sum(axis=0)[None, :] + 1e-12
+                got = o[b, :, h * d:(h + 1) * d]
+                assert np.all(np.abs(got - ex) <= bound)
+                assert np.abs(got - ex).max() > 1e-6       # the weights really are rounded
+                assert np.allclose(lse[b, h], logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+def test_attention_8bit_p_codes_against_torch():
+    """The FP8 weights: P_ij = E4M3(2^(t_ij - m_i)) with t the score in log2
+    units from the dequantised operands and m_i = ceil(max_j t_ij) - 7, an
+    integer; E4M3 rounding by torch's float8_e4m3fn. torch converts through
+    fp32, so pairs whose p lies within 1e-9 of a rounding boundary (or whose
+    fp32 value is one) are left out of the code comparison."""
+    B, L, H, d = 2, 200, 2, 64
+    q = RNG.standard_normal((B, L, H * d)) * np.array([1.0, 3.0])[:, None, None]
+    k, v = RNG.standard_normal((2, B, L, H * d))
+    k_lens = [200, 131]
+    seen = {}
+    O.attention_8bit(q, k, v, H, k_lens=k_lens,
+                     on_head=lambda b, h, z: seen.__setitem__((b, h), (z["t"], z["m"], z["p"],
+                                                                       z["P"])))
+    qd, kd, _ = _dequantised(q, k, v, H, k_lens)
+    e4 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn).double().numpy()
+    skipped = 0
+    for (b, h), (t_o, m_o, p_o, P_o) in seen.items():
+        n = k_lens[b]
+        t = qd[b, h] @ kd[b, h, :n].T / math.sqrt(d) / math.log(2.0)
+        m = np.ceil(t.max(axis=1)) - 7
+        p = np.exp2(t - m[:, None])
+        assert np.array_equal(m_o, m)
+        assert np.allclose(p_o, p, rtol=1e-12, atol=0)
+        assert np.all(p.max(axis=1) > 64) and np.all(p.max(axis=1) <= 128)
+        sure = e4(p * (1 - 1e-9)) == e4(p * (1 + 1e-9))
+        skipped += int((~sure).sum())
+        assert np.array_equal(P_o[sure], e4(p)[sure])
+    assert skipped < 50
+
+
+def test_attention_8bit_closed_forms():
+    B, L, H, d = 2, 150, 2, 32
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    # all scores equal (q = 0): every p is 2^7 exactly, so o is the mean of the
+    # dequantised values and lse = ln n
+    _, _, vd = O.quantize_v_mxfp8(v, H, lens=[150, 77])
+    oz, lz = O.attention_8bit(np.zeros_like(q), k, v, H, k_lens=[150, 77])
+    for b, n in enumerate((150, 77)):
+        for h in range(H):
+            assert np.allclose(oz[b, :, h * d:(h + 1) * d], vd[b, h, :n].mean(axis=0)[None, :],
+                               rtol=1e-14, atol=1e-15)
+        assert np.allclose(lz[b], np.log(n), rtol=0, atol=1e-13)
+    # one visible key: o = (E4M3(p) / p) v with p = 2^(t - ceil(t) + 7), lse = the score
+    o1, l1 = O.attention_8bit(q, k, v, H, k_lens=[1, 1])
+    qd, kd, vd1 = _dequantised(q, k, v, H, [1, 1])
     for b in range(B):
         for h in range(H):
-            S = (qc[b, h].astype(np.float64) * sq[b, h, blk][:, None]) @ \
-                (kc[b, h].astype(np.float64) * sk[b, h, blk][:, None]).T / np.sqrt(d)
-            w = np.exp(S - S.max(axis=1, keepdims=True))
-            od = (w @ vd[b, h]) / w.sum(axis=1, keepdims=True)
-            vmax = np.abs(vd[b, h]).max()
-            assert np.all(np.abs(o[b, :, h * d:(h + 1) * d] - od)
-                          <= 2 * (2 ** -4 + L * 2 ** -10) * vmax)
-    # all logits equal (q = 0): p = 2^7 exactly for every key, so o is the mean of the
-    # dequantised values
-    oz, lz = O.attention_8bit(np.zeros_like(q), k, v, H)
-    for h in range(H):
-        assert np.allclose(oz[:, :, h * d:(h + 1) * d], vd[:, h].mean(axis=1, keepdims=True),
-                           rtol=0, atol=1e-12)
-    assert np.allclose(lz, np.log(L))
-    # a single visible key returns its dequantised value exactly
-    o1k, _ = O.attention_8bit(q, k, v, H, k_lens=[1, 1])
-    for h in range(H):
-        assert np.array_equal(o1k[:, :, h * d:(h + 1) * d],
-                              np.broadcast_to(vd[:, h, :1], (B, L, d)))
-    # key lengths: k_len 0 gives zeros and -inf; keys in blocks wholly past k_len do nothing
-    o0, l0 = O.attention_8bit(q, k, v, H, k_lens=[0, 128])
+            s = qd[b, h] @ kd[b, h, 0] / math.sqrt(d)
+            t = s / math.log(2.0)
+            p = np.exp2(t - np.ceil(t) + 7)
+            ratio = O.e4m3_bits_to_f64(O.f64_to_e4m3_bits(p)) / p
+            assert np.allclose(o1[b, :, h * d:(h + 1) * d], ratio[:, None] * vd1[b, h, 0],
+                               rtol=1e-12, atol=1e-15)
+            assert np.allclose(l1[b, h], s, rtol=0, atol=1e-12)
+    # k_len 0: zeros and -inf
+    o0, l0 = O.attention_8bit(q, k, v, H, k_lens=[0, 150])
     assert not o0[0].any() and np.all(np.isneginf(l0[0]))
+
+
+def test_attention_8bit_keys_past_length_take_no_part():
+    """Non-finite or huge keys and values at or past k_len change nothing."""
+    B, L, H, d = 2, 150, 2, 32
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    o, lse = O.attention_8bit(q, k, v, H, k_lens=[100, 61])
     k2, v2 = k.copy(), v.copy()
-    k2[1, 128:] = 9.0
-    v2[1, 128:] = -7.0
-    o1, _ = O.attention_8bit(q, k2, v2, H, k_lens=[0, 128])
-    assert np.array_equal(o0[1], o1[1])
+    k2[0, 100:] = np.inf
+    v2[0, 100:] = np.nan
+    k2[1, 61:] = 1e4
+    v2[1, 61:] = -3e4
+    o2, lse2 = O.attention_8bit(q, k2, v2, H, k_lens=[100, 61])
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_attention_8bit_scalar_loops():
+    """Vectorised indexing (row and key blocks, heads, rows subset) against a
+    scalar loop over the same steps (tiny inputs; a consistency check, the
+    pins above tie the steps to exact attention and torch's E4M3)."""
+    B, L, H, d = 1, 70, 2, 16
+    q, k, v = RNG.standard_normal((3, B, L, H * d))
+    rows = np.array([0, 5, 63, 64, 69])
+    o, lse = O.attention_8bit(q, k, v, H, k_lens=[61], scale=0.3, rows=rows)
+    qc, sq = O.quantize_int8_blocks(q, H)
+    kc, sk = O.quantize_int8_blocks(k, H, lens=[61])
+    _, _, vd = O.quantize_v_mxfp8(v, H, lens=[61])
+    for h in range(H):
+        for r, i in enumerate(rows):
+            ts = []
+            for j in range(61):
+                S = sum(int(qc[0, h, i, e]) * int(kc[0, h, j, e]) for e in range(d))
+                ts.append(S * float(sq[0, h, i // 64]) * float(sk[0, h, j // 64]) * 0.3
+                          / math.log(2.0))
+            m = math.ceil(max(ts)) - 7
+            num, den = np.zeros(d), 0.0
+            for j, t in enumerate(ts):
+                p = 2.0 ** (t - m)
+                num += float(O.e4m3_bits_to_f64(O.f64_to_e4m3_bits(p))) * vd[0, h, j]
+                den += p
+            assert np.allclose(o[0, r, h * d:(h + 1) * d], num / den, rtol=1e-12, atol=1e-14)
+            assert abs(lse[0, h, r] - math.log(2.0) * (m + math.log2(den))) < 1e-12
