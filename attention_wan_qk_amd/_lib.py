@@ -5,9 +5,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-# WANATTN_LIB points the binding at another build of the same library.
-LIB_PATH = os.environ.get("WANATTN_LIB") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libwanattn.so")
+# The binding only ever loads the in-tree build next to this file.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwanattn.so")
 
 WAN_SUCCESS = 0
 WAN_ERROR_INVALID_VALUE = 1
@@ -38,8 +37,8 @@ SIGNATURES = {
     "wan_adaln_modulate_gate": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _F,
                                      _P]),
     "wan_linear_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _P]),
-    "wan_quantize_qkv_8bit": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L,
-                                   _L, _P]),
+    "wan_quantize_qkv_8bit": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L,
+                                   _L, _L, _P]),
     "wan_self_attn_fwd_8bit": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L,
                                     _F, _P]),
 }

@@ -23,15 +23,19 @@
 //  * The running maximum m is an integer (log2 units): P = 2^(t - m) is then
 //    the exact-maximum P times a power of two, so its E4M3 rounding does not
 //    depend on when m was last raised, and the rescale factor 2^(m - m') is
-//    exact. m is raised to ceil(max) - 7 when a row's maximum passes m + 8,
-//    so P stays below 2^8 (E4M3 reaches 448).
+//    exact. The tile maximum is only formed on a row's first tile and when a
+//    lane's sum of its 32 weights passes 448, E4M3's largest value (which
+//    any weight above 448 causes); then m is raised to ceil(max) - 7 if the
+//    maximum passes m + 8, and the tile's weights are formed and converted
+//    again. So every converted weight is at most 448, and m trails the
+//    exact-maximum offset by at most 3.
 //  * O^T += V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands:
 //    V^T fragments straight from the transposed tile, P from the softmax
 //    registers (v_cvt_pk_fp8_f32, round to nearest even), the V block scales
 //    applied by the MFMA itself (one E8M0 byte per lane, selected by op_sel).
-//  * The row sum l is the sum of the rounded P, formed by one more FP8 MFMA
-//    per tile (an all-ones A operand against P) instead of 32 VALU additions
-//    per lane: the softmax phase, not the MFMA pipe, bounds this kernel.
+//  * The softmax denominator l sums the unrounded fp32 weights (the FP8
+//    rounding belongs to the operand of the P V product only); each lane
+//    keeps four partial sums, combined across the two half-waves at the end.
 #include "wan_device.h"
 #include "wan_internal.h"
 
@@ -50,6 +54,7 @@ constexpr int kMaxBlocks = 4096;             // key-block scales kept in LDS (L 
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLoadsPerWave = kKTile / 1024 / (kWaves / 2);   // group-0 waves
 constexpr float kRescaleThreshold = 8.0f;
+constexpr float kSumLimit = 448.0f;          // per-lane tile sum of P that forces the tile max
 constexpr float kBias = 12582912.0f;         // 2^23 + 2^22
 constexpr int kBiasBits = 0x4B400000;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -189,12 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m_used = -INFINITY;
-  f32x16 lacc;                                // row sums of P (every element of a lane)
-#pragma unroll
-  for (int v = 0; v < 16; ++v) lacc[v] = 0.f;
-  // E4M3 1.0 in every byte: the A operand that turns the P V product into row sums
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};         // partial row sums of the unrounded P
   i32x16 s[2];
   i32x8 pq;                                   // P of the tile as 32 E4M3 bytes
 
@@ -216,7 +216,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
                                                                0, 127);                      \
   }
       WAN_PV(0) WAN_PV(1) WAN_PV(2) WAN_PV(3)
-      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pq, lacc, 0, 0, 0, 127, 0, 127);
 #undef WAN_PV
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
 #pragma unroll
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
     }
     if (jj < nT) {
       const char* Kt = Ks + KS * kKTile;
@@ -272,37 +271,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
       for (int e = 0; e < 32; ++e)
         if (jj * kBN + (e >> 4) * 32 + 16 * hf + (e & 15) >= kv_len) x[e] = -INFINITY;
     }
-    float mx = fmaxf(x[0], x[1]);
+    // P = 2^(t - m): per-lane partial sums of the fp32 values, and their E4M3
+    // codes (a weight above 448 converts to NaN; the sum check below then
+    // sends the tile through the exact path, which converts it again)
+    float sg[4];
+    auto exps = [&]() __attribute__((always_inline)) {
+      const float cc = -(kBias * mult) - m_used;
 #pragma unroll
-    for (int e = 2; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = (mx - kBias) * mult;     // row maximum in log2 units (exact offset)
-    if (__any(mt > m_used + kRescaleThreshold)) {
-      const float mn = fmaxf(m_used, ceilf(mt) - 7.0f);
-      const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
+      for (int i = 0; i < 4; ++i) sg[i] = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) lacc[v] *= alpha;
+      for (int q4 = 0; q4 < 8; ++q4) {
+        float p[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
-      m_used = mn;
-    }
-    const float cc = -(kBias * mult) - m_used;
-#pragma unroll
-    for (int q4 = 0; q4 < 8; ++q4) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + e], mult, cc));
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + e], mult, cc));
+          sg[e] += p[e];
+        }
+        const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        pq[q4] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
       }
-      uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      pq[q4] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+    };
+    bool exact = __any(m_used == -INFINITY);
+    if (!exact) {
+      exps();
+      const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));
+      exact = __any(!(big <= kSumLimit));
     }
+    if (exact) {
+      float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+      for (int e = 2; e < 32; ++e) mx = fmaxf(mx, x[e]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mt = (mx - kBias) * mult;   // row maximum in log2 units (exact offset)
+      if (__any(mt > m_used + kRescaleThreshold)) {
+        const float mn = fmaxf(m_used, ceilf(mt) - 7.0f);
+        const float alpha = mn == m_used ? 1.0f : __builtin_amdgcn_exp2f(m_used - mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ls[i] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+        m_used = mn;
+      }
+      exps();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ls[i] += sg[i];
   };
 
   // As in the bf16 kernel: tile j's K and tile j-1's V (with its scale
@@ -341,7 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
     phase_barrier();
   }
 
-  const float lsum = lacc[0];
+  float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                     false, false);
+    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (qrow < a.L) {
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.L + qrow) * a.ld_o + h * kHD;

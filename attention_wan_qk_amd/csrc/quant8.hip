@@ -13,7 +13,10 @@
 //    E4M3(clamp(v / X, +-448)) rounded to nearest even. Stored transposed
 //    per block (D rows of 64 key bytes), the A-operand layout of the P V
 //    product, with the scale bytes ordered as the MFMA reads them.
-//  * Rows past L are quantised as zeros. Key lengths play no part here.
+//  * Rows past L are quantised as zeros, and so are key and value rows at or
+//    past k_lens[b]: padding takes no part in attention, so it must not set
+//    the block scales of the valid keys (nor carry an inf or NaN into them).
+//    Query rows are all quantised.
 // Memory-bound: 2 + 2 + 2 bytes read and 1 + 1 + 1 written per element of
 // q, k and v.
 #include "wan_device.h"
@@ -85,13 +88,16 @@ __global__ __launch_bounds__(kThreads) void quant8_kernel(Quant8Args a) {
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int rows = min(kBlock, a.L - blk * kBlock);
+  int kv_len = a.L;
+  if (a.k_lens) kv_len = min(max(a.k_lens[b], 0), a.L);
+  const int rows_kv = max(0, min(rows, kv_len - blk * kBlock));   // valid key rows of the block
   const int64_t tok0 = (int64_t)b * a.L + (int64_t)blk * kBlock;
   const int64_t tile = (int64_t)bh * nT + blk;   // [B][H][nT]
 
   quant_int8(a.q8 + tile * kBlock * kHD, a.q_scale + tile,
              static_cast<const uint16_t*>(a.q) + tok0 * a.ld_q + h * kHD, a.ld_q, rows, red);
   quant_int8(a.k8 + tile * kBlock * kHD, a.k_scale + tile,
-             static_cast<const uint16_t*>(a.k) + tok0 * a.ld_k + h * kHD, a.ld_k, rows, red);
+             static_cast<const uint16_t*>(a.k) + tok0 * a.ld_k + h * kHD, a.ld_k, rows_kv, red);
 
   // v: stage the block in LDS, then thread t owns channel t % 128 of key
   // half t / 128 (32 keys).
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void quant8_kernel(Quant8Args a) {
     for (int i = 0; i < 4; ++i) {
       const int r = (t >> 4) + 16 * i;
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (r < rows) w = load_stream(vin + (int64_t)r * a.ld_v + 8 * (t & 15));
+      if (r < rows_kv) w = load_stream(vin + (int64_t)r * a.ld_v + 8 * (t & 15));
       *reinterpret_cast<u32x4*>(vt + r * kHD + 8 * (t & 15)) = w;
     }
   }

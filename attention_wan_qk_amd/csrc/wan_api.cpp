@@ -361,8 +361,9 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w, const float* b
 
 wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8, float* q_scale,
                                   float* k_scale, uint8_t* v_scale, const void* q, const void* k,
-                                  const void* v, int B, int L, int H, int D, int64_t ld_q,
-                                  int64_t ld_k, int64_t ld_v, hipStream_t stream) {
+                                  const void* v, const int32_t* k_lens, int B, int L, int H,
+                                  int D, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                                  hipStream_t stream) {
   if (B < 0 || L < 0 || H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
   if (D != kHeadDim) return WAN_ERROR_NOT_SUPPORTED;
   if ((int64_t)B * L == 0) return WAN_SUCCESS;
@@ -395,7 +396,9 @@ wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8, float* q_
     for (int j = i + 1; j < 6; ++j)
       if (overlap(outs[i], outs[j])) return WAN_ERROR_INVALID_VALUE;
   }
-  wan::Quant8Args a{q8, k8, v8, q_scale, k_scale, v_scale, q, k, v, B, L, H, ld_q, ld_k, ld_v};
+  if (k_lens && (reinterpret_cast<uintptr_t>(k_lens) & 3u)) return WAN_ERROR_INVALID_VALUE;
+  wan::Quant8Args a{q8, k8, v8, q_scale, k_scale, v_scale, q, k, v, k_lens,
+                    B, L, H, ld_q, ld_k, ld_v};
   return from_hip(wan::launch_quant8(a, stream));
 }
 

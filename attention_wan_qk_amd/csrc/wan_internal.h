@@ -69,6 +69,7 @@ struct Quant8Args {
   const void* q;
   const void* k;
   const void* v;
+  const int32_t* k_lens;   // device [B] or NULL: key/value rows at or past it are zero
   int B, L, H;
   int64_t ld_q, ld_k, ld_v;
 };

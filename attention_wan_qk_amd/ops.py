@@ -3,6 +3,10 @@
 Each function only checks tensor metadata, allocates outputs with torch and
 passes raw device pointers, sizes, strides and the current HIP stream to the
 library. All arithmetic happens in the library's kernels.
+
+The C ABI sees pointers and sizes only, so every shape, stride and length a
+kernel relies on is checked here first (ValueError / TypeError), before the
+device check and before anything reaches the library.
 """
 
 from __future__ import annotations
@@ -25,8 +29,8 @@ def _ptr(t):
 def _token_major(t: torch.Tensor, name: str, C: int):
     """bf16 tensor [B, L, C] or [B, L, H, D] whose rows may be a column slice
     of a wider buffer. Returns (B, L, ld)."""
-    if t.dtype != torch.bfloat16 or not t.is_cuda:
-        raise TypeError(f"{name}: expected a bf16 CUDA tensor, got {t.dtype} on {t.device}")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: expected a bf16 tensor, got {t.dtype}")
     if t.dim() == 4:
         B, L, H, D = t.shape
         if H * D != C or t.stride(3) != 1 or t.stride(2) != D:
@@ -41,6 +45,28 @@ def _token_major(t: torch.Tensor, name: str, C: int):
     if B > 1 and t.stride(0) != L * ld:
         raise ValueError(f"{name}: batch stride must be L * row stride")
     return B, L, ld
+
+
+def _check_lens(lens, B: int, name: str) -> None:
+    """Per-sample lengths: a contiguous int32 tensor of B elements, or None."""
+    if lens is None:
+        return
+    if lens.dtype != torch.int32:
+        raise TypeError(f"{name} must be an int32 tensor")
+    if lens.numel() != B or not lens.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor of B = {B} lengths")
+
+
+def _same(name: str, got, want) -> None:
+    if tuple(got) != tuple(want):
+        raise ValueError(f"{name}: expected (B, L) = {tuple(want)}, got {tuple(got)}")
+
+
+def _on_device(*ts) -> None:
+    """Every tensor (None skipped) is on the same GPU."""
+    devs = {t.device for t in ts if t is not None}
+    if any(d.type != "cuda" for d in devs) or len(devs) != 1:
+        raise TypeError(f"tensors must all be on one CUDA device, got {sorted(map(str, devs))}")
 
 
 def _channels(t: torch.Tensor) -> int:
@@ -61,14 +87,26 @@ def qk_norm_rope3d(q, k, heads: int, grid, gain_q=None, gain_k=None, *, eps: flo
     if inplace:
         q_out, k_out = q, k
     else:
+        if (q_out is not None and q is None) or (k_out is not None and k is None):
+            raise ValueError("an output is given for a missing input")
         if q is not None and q_out is None:
             q_out = torch.empty(B, L, C, dtype=torch.bfloat16, device=ref.device)
         if k is not None and k_out is None:
             k_out = torch.empty(B, L, C, dtype=torch.bfloat16, device=ref.device)
-    ld_out = _token_major(q_out if q_out is not None else k_out, "out", C)[2]
+    outs = [(n, t) for n, t in (("q_out", q_out), ("k_out", k_out)) if t is not None]
+    ld_out = None
+    for n, t in outs:   # one row stride serves both outputs
+        Bo, Lo, ldo = _token_major(t, n, C)
+        _same(n, (Bo, Lo), (B, L))
+        if ld_out is not None and ldo != ld_out:
+            raise ValueError("q_out and k_out must share one row stride")
+        ld_out = ldo
     for g in (gain_q, gain_k):
         if g is not None and (g.dtype != torch.float32 or g.numel() != C or not g.is_contiguous()):
             raise ValueError("gains must be contiguous fp32 [H*D]")
+    if C % heads:
+        raise ValueError(f"{C} channels do not split into {heads} heads")
+    _on_device(q, k, q_out, k_out, gain_q, gain_k)
     flags = (WAN_NORM if norm else 0) | (WAN_ROPE if rope else 0) | \
         (WAN_NORM_PER_HEAD if per_head else 0)
     f, h, w = grid if grid is not None else (0, 0, 0)
@@ -84,14 +122,18 @@ def self_attn_fwd(q, k, v, heads: int, k_lens=None, scale: float = 0.0, out=None
     """Full non-causal self-attention; returns o (and lse [B, H, L] fp32)."""
     C = _channels(q)
     B, L, ld_q = _token_major(q, "q", C)
-    _, _, ld_k = _token_major(k, "k", C)
-    _, _, ld_v = _token_major(v, "v", C)
+    *bl, ld_k = _token_major(k, "k", C)
+    _same("k", bl, (B, L))
+    *bl, ld_v = _token_major(v, "v", C)
+    _same("v", bl, (B, L))
+    if out is not None:
+        _same("out", _token_major(out, "out", C)[:2], (B, L))
+    _check_lens(k_lens, B, "k_lens")
+    _on_device(q, k, v, out, k_lens)
     if out is None:
         out = torch.empty(B, L, C, dtype=torch.bfloat16, device=q.device)
     ld_o = _token_major(out, "out", C)[2]
     lse = torch.empty(B, heads, L, dtype=torch.float32, device=q.device) if return_lse else None
-    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
-        raise TypeError("k_lens must be a CUDA int32 tensor")
     st = lib().wan_self_attn_fwd(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(k_lens), B, L, heads, C // heads, ld_q, ld_k, ld_v,
                                  ld_o, scale, _stream(q))
@@ -103,15 +145,19 @@ def cross_attn_fwd(q, k, v, heads: int, context_lens=None, scale: float = 0.0, o
     """Cross-attention of q [B, Lq, C] to k, v [B, Lk, C]; returns o."""
     C = _channels(q)
     B, Lq, ld_q = _token_major(q, "q", C)
-    _, Lk, ld_k = _token_major(k, "k", C)
-    _, _, ld_v = _token_major(v, "v", C)
+    Bk, Lk, ld_k = _token_major(k, "k", C)
+    _same("k", (Bk,), (B,))
+    *bl, ld_v = _token_major(v, "v", C)
+    _same("v", bl, (B, Lk))
     if ld_k != ld_v:
         raise ValueError("k and v must share one row stride")
+    if out is not None:
+        _same("out", _token_major(out, "out", C)[:2], (B, Lq))
+    _check_lens(context_lens, B, "context_lens")
+    _on_device(q, k, v, out, context_lens)
     if out is None:
         out = torch.empty(B, Lq, C, dtype=torch.bfloat16, device=q.device)
     ld_o = _token_major(out, "out", C)[2]
-    if context_lens is not None and (context_lens.dtype != torch.int32 or not context_lens.is_cuda):
-        raise TypeError("context_lens must be a CUDA int32 tensor")
     st = lib().wan_cross_attn_fwd(_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(context_lens), B,
                                   Lq, Lk, heads, C // heads, ld_q, ld_k, ld_o, scale,
                                   _stream(q))
@@ -125,14 +171,18 @@ def chunk_causal_attn_fwd(q, k, v, heads: int, q_offset: int, chunk_len: int, k_
     where a key is visible iff its chunk is not after the query's chunk."""
     C = _channels(q)
     B, Lq, ld_q = _token_major(q, "q", C)
-    _, Lk, ld_k = _token_major(k, "k", C)
-    _, _, ld_v = _token_major(v, "v", C)
+    Bk, Lk, ld_k = _token_major(k, "k", C)
+    _same("k", (Bk,), (B,))
+    *bl, ld_v = _token_major(v, "v", C)
+    _same("v", bl, (B, Lk))
+    if out is not None:
+        _same("out", _token_major(out, "out", C)[:2], (B, Lq))
+    _check_lens(k_lens, B, "k_lens")
+    _on_device(q, k, v, out, k_lens)
     if out is None:
         out = torch.empty(B, Lq, C, dtype=torch.bfloat16, device=q.device)
     ld_o = _token_major(out, "out", C)[2]
     lse = torch.empty(B, heads, Lq, dtype=torch.float32, device=q.device) if return_lse else None
-    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
-        raise TypeError("k_lens must be a CUDA int32 tensor")
     st = lib().wan_chunk_causal_attn_fwd(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(k_lens), B, Lq, Lk, heads, C // heads, q_offset,
                                          chunk_len, ld_q, ld_k, ld_v, ld_o, scale, _stream(q))
@@ -145,8 +195,8 @@ def _mod_strides(vecs, B, L, C):
     for v in vecs:
         if v is None:
             continue
-        if v.dtype != torch.float32 or not v.is_cuda or v.stride(-1) != 1:
-            raise ValueError("modulation vectors must be fp32 CUDA tensors with unit channel stride")
+        if v.dtype != torch.float32 or v.stride(-1) != 1:
+            raise ValueError("modulation vectors must be fp32 tensors with unit channel stride")
         if v.dim() == 2 and tuple(v.shape) == (B, C):
             s = (v.stride(0) if B > 1 else C, 0)
         elif v.dim() == 3 and tuple(v.shape) == (B, L, C):
@@ -167,11 +217,15 @@ def adaln_modulate_gate(x, y=None, gate=None, shift=None, scale=None, eps: float
     B, L, C = x.shape
     if y is not None and (y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous()):
         raise ValueError("y must match x")
+    for n, t in (("x_out", x_out), ("h_out", h_out)):
+        if t is not None and (t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous bf16 tensor shaped like x")
+    sb, sl = _mod_strides((gate, shift, scale), B, L, C)
+    _on_device(x, y, gate, shift, scale, x_out, h_out)
     if want_x and x_out is None:
         x_out = torch.empty_like(x)
     if want_h and h_out is None:
         h_out = torch.empty_like(x)
-    sb, sl = _mod_strides((gate, shift, scale), B, L, C)
     st = lib().wan_adaln_modulate_gate(_ptr(x_out), _ptr(h_out), _ptr(x), _ptr(y), _ptr(gate),
                                        _ptr(shift), _ptr(scale), B, L, C, sb, sl, eps,
                                        _stream(x))
@@ -198,8 +252,8 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
 def linear_fwd(x, weight, bias=None, out=None):
     """y = x W^T + b for x [..., K] (rows may be a column slice of a wider
     buffer), weight [N, K] bf16, bias fp32 [N] or None; returns y [..., N]."""
-    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or not x.is_cuda:
-        raise TypeError("x and weight must be bf16 CUDA tensors")
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("x and weight must be bf16 tensors")
     K = x.shape[-1]
     N = weight.shape[0]
     if weight.dim() != 2 or weight.shape[1] != K or weight.stride(1) != 1:
@@ -212,10 +266,11 @@ def linear_fwd(x, weight, bias=None, out=None):
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or
                              not bias.is_contiguous()):
         raise ValueError("bias must be contiguous fp32 [N]")
+    if out is not None and (tuple(out.shape) != (*lead, N) or out.dtype != torch.bfloat16):
+        raise ValueError("out must be bf16 [..., N] matching x")
+    _on_device(x, weight, bias, out)
     if out is None:
         out = torch.empty(*lead, N, dtype=torch.bfloat16, device=x.device)
-    if tuple(out.shape) != (*lead, N) or out.dtype != torch.bfloat16:
-        raise ValueError("out must be bf16 [..., N] matching x")
     ld_y = _row_stride(out, "out")
     st = lib().wan_linear_fwd(_ptr(out), _ptr(x), _ptr(weight), _ptr(bias), M, N, K, ld_x,
                               weight.stride(0), ld_y, _stream(x))
@@ -223,10 +278,11 @@ def linear_fwd(x, weight, bias=None, out=None):
     return out
 
 
-def quantize_qkv_8bit(q, k, v, heads: int, out: dict | None = None):
+def quantize_qkv_8bit(q, k, v, heads: int, k_lens=None, out: dict | None = None):
     """INT8 q, k (per 64-token block) and MXFP8 v (per channel and 32 keys) in
-    the layouts the 8-bit attention reads; returns a dict of device tensors
-    (``out``, a dict returned by an earlier call of the same shape, is reused)."""
+    the layouts the 8-bit attention reads, key/value rows at or past k_lens
+    quantised as zeros; returns a dict of device tensors (``out``, a dict
+    returned by an earlier call of the same shape, is reused)."""
     C = _channels(q)
     B, L, ld_q = _token_major(q, "q", C)
     _, Lk, ld_k = _token_major(k, "k", C)
@@ -236,13 +292,18 @@ def quantize_qkv_8bit(q, k, v, heads: int, out: dict | None = None):
     D = C // heads
     nT = (L + 63) // 64
     dev = q.device
+    _check_lens(k_lens, B, "k_lens")
+    if C % heads:
+        raise ValueError(f"{C} channels do not split into {heads} heads")
+    _on_device(q, k, v, k_lens)
     if out is not None:
         if (out["B"], out["L"], out["H"], out["D"]) != (B, L, heads, D):
             raise ValueError("out was made for another shape")
         st = lib().wan_quantize_qkv_8bit(_ptr(out["q8"]), _ptr(out["k8"]), _ptr(out["v8"]),
                                          _ptr(out["q_scale"]), _ptr(out["k_scale"]),
-                                         _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v), B, L,
-                                         heads, D, ld_q, ld_k, ld_v, _stream(q))
+                                         _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(k_lens), B, L, heads, D, ld_q, ld_k, ld_v,
+                                         _stream(q))
         check("wan_quantize_qkv_8bit", st)
         return out
     out = {
@@ -256,8 +317,8 @@ def quantize_qkv_8bit(q, k, v, heads: int, out: dict | None = None):
     }
     st = lib().wan_quantize_qkv_8bit(_ptr(out["q8"]), _ptr(out["k8"]), _ptr(out["v8"]),
                                      _ptr(out["q_scale"]), _ptr(out["k_scale"]),
-                                     _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v), B, L, heads,
-                                     D, ld_q, ld_k, ld_v, _stream(q))
+                                     _ptr(out["v_scale"]), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(k_lens), B, L, heads, D, ld_q, ld_k, ld_v, _stream(q))
     check("wan_quantize_qkv_8bit", st)
     return out
 
@@ -267,12 +328,14 @@ def self_attn_fwd_8bit(qkv8: dict, k_lens=None, scale: float = 0.0, out=None,
     """Self-attention on the output of quantize_qkv_8bit; returns o (and lse)."""
     B, L, H, D = qkv8["B"], qkv8["L"], qkv8["H"], qkv8["D"]
     dev = qkv8["q8"].device
+    if out is not None:
+        _same("out", _token_major(out, "out", H * D)[:2], (B, L))
+    _check_lens(k_lens, B, "k_lens")
+    _on_device(qkv8["q8"], out, k_lens)
     if out is None:
         out = torch.empty(B, L, H * D, dtype=torch.bfloat16, device=dev)
     ld_o = _token_major(out, "out", H * D)[2]
     lse = torch.empty(B, H, L, dtype=torch.float32, device=dev) if return_lse else None
-    if k_lens is not None and (k_lens.dtype != torch.int32 or not k_lens.is_cuda):
-        raise TypeError("k_lens must be a CUDA int32 tensor")
     st = lib().wan_self_attn_fwd_8bit(_ptr(out), _ptr(lse), _ptr(qkv8["q8"]), _ptr(qkv8["k8"]),
                                       _ptr(qkv8["v8"]), _ptr(qkv8["q_scale"]),
                                       _ptr(qkv8["k_scale"]), _ptr(qkv8["v_scale"]), _ptr(k_lens),

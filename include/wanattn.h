@@ -280,8 +280,11 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
  *         power-of-two scale 2^e, e = floor(log2 amax) - 8 (OCP microscaling;
  *         the scale byte is e + 127, amax = 0 gives byte 0), element =
  *         E4M3(clamp(v / 2^e, +-448)) rounded to nearest even.
+ *   Keys and values at or past k_lens[b] are padding: they are quantised as
+ *         zeros and left out of their blocks' scales.
  *   P:    E4M3 of 2^(t - m), t the scaled score in log2 units and m an integer
- *         running maximum; the softmax denominator sums the rounded P.
+ *         running maximum; the softmax denominator sums the unrounded
+ *         2^(t - m) in fp32 (only the operand of the P V product is FP8).
  * Quantised layouts (nT = ceil(L / 64); rows past L are zero):
  *   q8, k8   int8  [B][H][nT][64][D]          (token blocks, row-major)
  *   q_scale, k_scale  fp32 [B][H][nT]
@@ -294,7 +297,11 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
 /*
  * wan_quantize_qkv_8bit: quantise q, k, v ([B, L, H, D] bf16, row strides
  * ld_q, ld_k, ld_v; ld = 0 means H*D) into the layouts above. Outputs must
- * not overlap each other or the inputs. Key lengths play no part.
+ * not overlap each other or the inputs. k_lens: device int32 [B] or NULL
+ * (= L), clamped to [0, L]; key and value rows at or past it are never read
+ * (they may hold anything, inf and NaN included) and quantise as zeros.
+ * Pass the same k_lens to wan_self_attn_fwd_8bit. All query rows are
+ * quantised: a non-finite q value spoils the scale of its 64-row block.
  * Errors: WAN_ERROR_INVALID_VALUE for NULL/misaligned pointers, bad sizes or
  * strides, overlaps; WAN_ERROR_NOT_SUPPORTED for D != 128, H*D > 2^24, or
  * B*H*nT > 2^31 - 1 (one workgroup per block).
@@ -302,8 +309,9 @@ wanStatus_t wan_linear_fwd(void* y, const void* x, const void* w,
 wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
                                   float* q_scale, float* k_scale,
                                   uint8_t* v_scale, const void* q,
-                                  const void* k, const void* v, int B, int L,
-                                  int H, int D, int64_t ld_q, int64_t ld_k,
+                                  const void* k, const void* v,
+                                  const int32_t* k_lens, int B, int L, int H,
+                                  int D, int64_t ld_q, int64_t ld_k,
                                   int64_t ld_v, hipStream_t stream);
 
 /*
@@ -311,9 +319,9 @@ wanStatus_t wan_quantize_qkv_8bit(int8_t* q8, int8_t* k8, uint8_t* v8,
  * quantised k, v (all L tokens, keys masked by k_lens as in
  * wan_self_attn_fwd):
  *   S_ij = sum_d q8_id k8_jd (exact), mult = sq_i sk_j scale log2(e),
- *   m_i integer, P_ij = E4M3(2^(S_ij mult - m_i)),
- *   o_i = sum_j P_ij v_j / sum_j P_ij  (v dequantised),
- *   lse_i = ln 2 (m_i + log2 sum_j P_ij).
+ *   m_i integer, p_ij = 2^(S_ij mult - m_i), P_ij = E4M3(p_ij),
+ *   o_i = sum_j P_ij v_j / sum_j p_ij  (v dequantised),
+ *   lse_i = ln 2 (m_i + log2 sum_j p_ij).
  * INT8 MFMA for S, FP8 MFMA with hardware block scales for P V, fp32
  * accumulation; o is stored as bf16.
  * o      bf16 [B, L, H, D], row stride ld_o; must not overlap the inputs.

@@ -109,12 +109,13 @@ def p_code_spread(z: dict) -> np.ndarray:
         is how an fp32 value of the INT8 accumulator offset by 2^23 + 2^22
         is cancelled;
       * 2^-24 |t_ij - m_i| (the fused multiply-add) and 2^-22 (exp2 to one ulp).
-    Its integer offset may also sit at m - 2 .. m + 1 (the running maximum is
-    only raised once a score passes it by more than 8, and the ceiling is
-    taken of an fp32 maximum), which multiplies every weight by 2^s,
-    s in {-1, 0, 1, 2}: that leaves normal E4M3 roundings unchanged and moves
-    only weights below 2^-4 (subnormal under some s). The spread is the
-    largest minus the smallest E4M3 value among those choices.
+    Its integer offset may also sit at m - 3 .. m + 1: a streaming evaluation
+    need only raise its running offset before a weight would pass 448,
+    E4M3's largest value (448 < 2^9, and the offset it then takes is the
+    ceiling of an fp32 maximum, minus 7). That multiplies every weight by
+    2^s, s in {-1, 0, 1, 2, 3}, which leaves normal E4M3 roundings unchanged
+    and moves only weights below 2^-4 (subnormal under some s). The spread is
+    the largest minus the smallest E4M3 value among those choices.
     """
     t, m, p, unit = z["t"], z["m"], z["p"], z["unit"]
     eps = (2.0 ** -20 * np.abs(t) + unit + 2.0 ** -24 * (np.abs(m)[:, None] + 1)
@@ -126,7 +127,7 @@ def p_code_spread(z: dict) -> np.ndarray:
     if small.any():
         ps, fs = p[small], f[small]
         c = [lo[small], hi[small]]
-        for s in (-1, 1, 2):
+        for s in (-1, 1, 2, 3):
             k = 2.0 ** s
             c += [_e4m3(ps * k / fs) / k, _e4m3(ps * k * fs) / k]
         c = np.stack(c)
