@@ -42,6 +42,13 @@
 //    global chunk that belongs there.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
+//  * With a workspace (self-attention), the work items of the last, partly
+//    filled round of the chip are split into key ranges run by otherwise idle
+//    CUs; each range leaves its unnormalised output, running max and sum, and
+//    a second kernel combines them (the partial softmax results of disjoint
+//    key sets merge exactly through their maxima).
+#include <mutex>
+
 #include "wan_device.h"
 #include "wan_internal.h"
 
@@ -54,6 +61,7 @@ constexpr int kAheadV = 4;                   // V fragments read ahead of their 
 constexpr int kAheadK = 4;                   // K fragments read ahead of their MFMAs
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
+static_assert(kBM == kAttnRows && kBN == kAttnKeys, "tiling shared with the host-side planning");
 constexpr int kKB = kBN / 32;                // 32-key blocks per tile
 constexpr int kKC = kBN / 16;                // 16-key chunks per tile (PV k-steps)
 constexpr int kHD = 128;                     // head size
@@ -130,8 +138,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   // them, one per CU): with only a few key tiles per query tile, launching a
   // workgroup per tile costs a noticeable share of its short life. The other
   // kinds run one item per workgroup.
+  const bool kSplitting = kKind == 0 && a.part != nullptr;
   for (uint32_t item = blockIdx.x;;) {
-    const uint32_t logical = xcd_remap(item, total);
+    // Key-split workgroups (after the n_full whole items) take range
+    // split % n_split of item n_full + split / n_split.
+    const int split = kSplitting && item >= a.n_full ? (int)(item - a.n_full) : -1;
+    const uint32_t logical = split >= 0 ? a.n_full + split / a.n_split
+                                        : xcd_remap(item, kSplitting ? a.n_full : total);
     const int qt = logical % nQ;
     const int bh = logical / nQ;
     const int h = bh % a.H;
@@ -150,7 +163,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     };
     const int lim_lo = key_limit(min(qt * kBM, a.Lq - 1));
     const int lim_hi = key_limit(min(qt * kBM + kBM - 1, a.Lq - 1));
-    const int nT = (lim_hi + kBN - 1) / kBN;
+    // This workgroup streams key tiles t0 .. t0 + nT - 1.
+    int t0 = 0, nT = (lim_hi + kBN - 1) / kBN;
+    if (split >= 0) {
+      const int sp = split % a.n_split, all = nT;
+      t0 = (int)((int64_t)all * sp / a.n_split);
+      nT = (int)((int64_t)all * (sp + 1) / a.n_split) - t0;
+    }
 
     const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.Lq * a.ld_q + h * kHD;
     const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)b * a.Lk * a.ld_k + h * kHD;
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       vo_v[i] = r * row_v + (v_phys(r, p) << 4);
     }
     auto dma_k = [&](int t, int slot) {
-      const uint32_t sk = (uint32_t)t * kBN * row_k;
+      const uint32_t sk = (uint32_t)(t0 + t) * kBN * row_k;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             vo_k[i], sk, 0, 0);
     };
     auto dma_v = [&](int t, int slot) {
-      const uint32_t sv = (uint32_t)t * kBN * row_v;
+      const uint32_t sv = (uint32_t)(t0 + t) * kBN * row_v;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -294,12 +313,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     // Softmax phase of tile jj: running max/sum update and P = exp2(...) as bf16.
     auto softmax = [&](int jj) {
       if (jj < 0 || jj >= nT) return;
-      if ((jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
+      if ((t0 + jj + 1) * kBN > lim_lo) {   // keys past this row's limit (last tiles only)
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = jj * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+            const int key = (t0 + jj) * kBN + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
             if (key >= lim_row) s[kb][v] = -INFINITY;
           }
       }
@@ -409,7 +428,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                                                        false, false);
       lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (qrow < a.Lq) {
+    if (split >= 0) {
+      // partial result of this key range: O unnormalised (relative to m),
+      // then m and l per row; rows past Lq are written too and never read
+      float* pp = a.part + (int64_t)split * kAttnPartFloats;
+      const int prow = wave * 32 + r32;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<f32x4*>(pp + prow * kHD + 32 * db + 8 * a4 + 4 * hf) =
+              f32x4{oacc[db][4 * a4], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2],
+                    oacc[db][4 * a4 + 3]};
+      if (hf == 0) {
+        pp[kBM * kHD + prow] = m_used;
+        pp[kBM * kHD + kBM + prow] = lsum;
+      }
+    } else if (qrow < a.Lq) {
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
       uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
 #pragma unroll
@@ -435,6 +470,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Combines the key-split partial results of the last work items: for query
+// row i with ranges s, M = max_s m_s, w_s = 2^(m_s - M), o_i = sum_s w_s O_s /
+// sum_s w_s l_s and lse = M ln 2 + ln(sum_s w_s l_s) (no visible key: o = 0,
+// lse = -inf). One thread per (row, 4 channels), 8 rows per block.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int nQ = (a.Lq + kBM - 1) / kBM;
+  const int64_t t = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // tail row
+  const int c4 = threadIdx.x & 31;                                   // channels 4 c4 .. +3
+  const int tail_item = (int)(t / kBM), prow = (int)(t % kBM);
+  const uint32_t logical = a.n_full + tail_item;
+  const int qt = logical % nQ, bh = logical / nQ, h = bh % a.H, b = bh / a.H;
+  const int qrow = qt * kBM + prow;
+  if (qrow >= a.Lq) return;
+  const float* base = a.part + (int64_t)tail_item * a.n_split * kAttnPartFloats;
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.n_split; ++sp)
+    M = fmaxf(M, base[sp * kAttnPartFloats + kBM * kHD + prow]);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float* pp = base + sp * kAttnPartFloats;
+    const float ms = pp[kBM * kHD + prow];
+    if (ms == -INFINITY) continue;   // no visible key in this range
+    const float w = __builtin_amdgcn_exp2f(ms - M);
+    l += w * pp[kBM * kHD + kBM + prow];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(pp + prow * kHD + 4 * c4);
+    acc += w * os;
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 y = __builtin_convertvector(acc * inv, bf16x4);
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
+  *reinterpret_cast<u32x2*>(orow + 4 * c4) = __builtin_bit_cast(u32x2, y);
+  if (a.lse && c4 == 0)
+    a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
+        l > 0.f ? M * 0.6931471805599453f + logf(l) : -INFINITY;
+}
+
 hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s) {
   const int nQ = (a.Lq + kBM - 1) / kBM;
   const int64_t total = (int64_t)a.B * a.H * nQ;
@@ -442,7 +515,19 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s) {
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(kThreads);
   switch (kind) {
-    case 0: hipLaunchKernelGGL(attn_fwd_kernel<0>, grid, block, 0, s, a); break;
+    case 0:
+      if (a.part) {
+        const int64_t tail = total - a.n_full;
+        if (tail <= 0 || a.n_split < 2) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(attn_fwd_kernel<0>, dim3((unsigned)(a.n_full + tail * a.n_split)), block,
+                           0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(tail * kBM / 8)), dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(attn_fwd_kernel<0>, grid, block, 0, s, a);
+      }
+      break;
     case 1:
       hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3((unsigned)(total < 256 ? total : 256)), block, 0,
                          s, a);
@@ -451,6 +536,30 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int kind, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_device_mutex;
+int g_cus[kMaxDevices];                 // 0: not looked up yet
+
+}  // namespace
+
+hipError_t device_cu_count(int* n) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_device_mutex);
+  if (g_cus[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus[dev] = cus;
+  }
+  *n = g_cus[dev];
+  return hipSuccess;
 }
 
 }  // namespace wan

@@ -184,19 +184,26 @@ wanStatus_t wan_qk_norm_rope3d(void* q_out, void* k_out, const void* q, const vo
   return from_hip(wan::launch_norm_rope(a, stream));
 }
 
-wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k, const void* v,
-                              const int32_t* k_lens, int B, int L, int H, int D, int64_t ld_q,
-                              int64_t ld_k, int64_t ld_v, int64_t ld_o, float softmax_scale,
-                              hipStream_t stream) {
-  if (B < 0 || L < 0) return WAN_ERROR_INVALID_VALUE;
-  if ((int64_t)B * L == 0) {
-    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
-    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
-  }
-  wanStatus_t st = check_attn(o, lse, q, k, v, B, L, L, H, D, ld_q, ld_k, ld_v, ld_o,
-                              softmax_scale);
-  if (st != WAN_SUCCESS) return st;
-  wan::AttnArgs a;
+}  // extern "C"
+
+namespace {
+
+// Key split of a self-attention call on the current device (no split if the
+// device cannot be queried).
+wan::AttnSplit self_attn_split(int B, int L, int H) {
+  int cus = 0;
+  if (wan::device_cu_count(&cus) != hipSuccess) cus = 0;
+  const int64_t items = (int64_t)B * H * ((L + wan::kAttnRows - 1) / wan::kAttnRows);
+  return wan::plan_self_attn_split(items, (L + wan::kAttnKeys - 1) / wan::kAttnKeys, cus);
+}
+
+// Self-attention with the argument checks of check_attn; `part` (NULL: no
+// split) receives the key-split partial results planned by `split`.
+wanStatus_t self_attn(void* o, float* lse, const void* q, const void* k, const void* v,
+                      const int32_t* k_lens, int B, int L, int H, int64_t ld_q, int64_t ld_k,
+                      int64_t ld_v, int64_t ld_o, float softmax_scale, float* part,
+                      const wan::AttnSplit& split, hipStream_t stream) {
+  wan::AttnArgs a{};
   a.o = o;
   a.lse = lse;
   a.q = q;
@@ -211,11 +218,76 @@ wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k,
   a.ld_k = ld_k;
   a.ld_v = ld_v;
   a.ld_o = ld_o;
-  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   a.scale_log2 = sc * 1.4426950408889634f;
   a.q_offset = 0;
   a.chunk_len = 0;
+  a.part = part;
+  a.n_full = split.n_full;
+  a.n_split = split.n_split;
   return from_hip(wan::launch_attn_fwd(a, 0, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q, const void* k, const void* v,
+                              const int32_t* k_lens, int B, int L, int H, int D, int64_t ld_q,
+                              int64_t ld_k, int64_t ld_v, int64_t ld_o, float softmax_scale,
+                              hipStream_t stream) {
+  if (B < 0 || L < 0) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * L == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  wanStatus_t st = check_attn(o, lse, q, k, v, B, L, L, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  const wan::AttnSplit none{(uint32_t)((int64_t)B * H * ((L + wan::kAttnRows - 1) / wan::kAttnRows)),
+                            1, 0};
+  return self_attn(o, lse, q, k, v, k_lens, B, L, H, ld_q, ld_k, ld_v, ld_o, softmax_scale,
+                   nullptr, none, stream);
+}
+
+size_t wan_self_attn_workspace_size(int B, int L, int H, int D) {
+  if (B < 1 || L < 1 || H < 1 || D != kHeadDim) return 0;
+  return (size_t)self_attn_split(B, L, H).bytes;
+}
+
+wanStatus_t wan_self_attn_fwd_ws(void* o, float* lse, const void* q, const void* k,
+                                 const void* v, const int32_t* k_lens, int B, int L, int H,
+                                 int D, int64_t ld_q, int64_t ld_k, int64_t ld_v, int64_t ld_o,
+                                 float softmax_scale, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (B < 0 || L < 0) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * L == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  wanStatus_t st = check_attn(o, lse, q, k, v, B, L, L, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  const wan::AttnSplit split = self_attn_split(B, L, H);
+  float* part = nullptr;
+  if (split.bytes > 0) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < split.bytes)
+      return WAN_ERROR_INVALID_VALUE;
+    const int64_t C = (int64_t)H * D, rows = (int64_t)B * L;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace);
+    const Range rw{lo, lo + (uintptr_t)split.bytes};
+    if (overlap(rw, span_bf16(o, rows, ld_o, C)) || overlap(rw, span_bf16(q, rows, ld_q, C)) ||
+        overlap(rw, span_bf16(k, rows, ld_k, C)) || overlap(rw, span_bf16(v, rows, ld_v, C)))
+      return WAN_ERROR_INVALID_VALUE;
+    if (lse) {
+      const uintptr_t ll = reinterpret_cast<uintptr_t>(lse);
+      if (overlap(rw, Range{ll, ll + (uintptr_t)((int64_t)B * H * L * 4)}))
+        return WAN_ERROR_INVALID_VALUE;
+    }
+    part = static_cast<float*>(workspace);
+  }
+  return self_attn(o, lse, q, k, v, k_lens, B, L, H, ld_q, ld_k, ld_v, ld_o, softmax_scale,
+                   part, split, stream);
 }
 
 wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void* v,
@@ -231,7 +303,7 @@ wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void
   wanStatus_t st = check_attn(o, nullptr, q, k, v, B, Lq, Lk, H, D, ld_q, ld_k, ld_v, ld_o,
                               softmax_scale);
   if (st != WAN_SUCCESS) return st;
-  wan::AttnArgs a;
+  wan::AttnArgs a{};
   a.o = o;
   a.lse = nullptr;
   a.q = q;
@@ -266,7 +338,7 @@ wanStatus_t wan_chunk_causal_attn_fwd(void* o, float* lse, const void* q, const 
   wanStatus_t st = check_attn(o, lse, q, k, v, B, Lq, Lk, H, D, ld_q, ld_k, ld_v, ld_o,
                               softmax_scale);
   if (st != WAN_SUCCESS) return st;
-  wan::AttnArgs a;
+  wan::AttnArgs a{};
   a.o = o;
   a.lse = lse;
   a.q = q;

@@ -48,7 +48,48 @@ struct AttnArgs {
   float scale_log2;   // softmax scale * log2(e)
   int q_offset;       // chunk-causal only: global position of query row 0
   int chunk_len;      // chunk-causal only: tokens per chunk (>= 1)
+  // Self-attention only: when part is not NULL, work items n_full and later
+  // are split into n_split key ranges whose partial results go to part and
+  // are combined by a second kernel (see plan_self_attn_split).
+  float* part;
+  uint32_t n_full;
+  int n_split;
 };
+
+// Self-attention work items are 256 query rows of one (batch, head); keys are
+// streamed in tiles of 64.
+constexpr int kAttnRows = 256;
+constexpr int kAttnKeys = 64;
+// Floats of one key-split partial result: O [256][128] unnormalised, then
+// the running maximum m [256] (log2 units) and the sum l [256].
+constexpr uint64_t kAttnPartFloats = (uint64_t)kAttnRows * 128 + 2 * kAttnRows;
+
+// Key split of the last round of self-attention work items. With `items`
+// items of `n_tiles` key tiles each and one item per CU at a time, the last
+// items % cus items would run on a partly idle chip; when they are at most
+// half of it, each is split into n_split key ranges instead (up to one per
+// idle CU), whose partial results need `bytes` of workspace. n_split = 1:
+// no split.
+struct AttnSplit {
+  uint32_t n_full;
+  int n_split;
+  uint64_t bytes;
+};
+
+inline AttnSplit plan_self_attn_split(int64_t items, int n_tiles, int cus) {
+  AttnSplit none{(uint32_t)items, 1, 0};
+  if (cus <= 0 || n_tiles < 32 || items <= 0) return none;
+  const int64_t tail = items % cus;
+  if (tail == 0 || 2 * tail > cus) return none;
+  int64_t split = cus / tail;
+  if (split > n_tiles) split = n_tiles;
+  if (split < 2) return none;
+  return AttnSplit{(uint32_t)(items - tail), (int)split,
+                   (uint64_t)(tail * split) * kAttnPartFloats * 4};
+}
+
+// Compute units of the current device (cached per device).
+hipError_t device_cu_count(int* n);
 
 struct LinearArgs {
   void* y;

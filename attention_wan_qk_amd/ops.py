@@ -134,10 +134,15 @@ def self_attn_fwd(q, k, v, heads: int, k_lens=None, scale: float = 0.0, out=None
         out = torch.empty(B, L, C, dtype=torch.bfloat16, device=q.device)
     ld_o = _token_major(out, "out", C)[2]
     lse = torch.empty(B, heads, L, dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib().wan_self_attn_fwd(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(k_lens), B, L, heads, C // heads, ld_q, ld_k, ld_v,
-                                 ld_o, scale, _stream(q))
-    check("wan_self_attn_fwd", st)
+    # workspace for the key split of the last round of work (torch's caching
+    # allocator keeps it stream-ordered and cheap after the first call)
+    with torch.cuda.device(q.device):
+        ws_bytes = lib().wan_self_attn_workspace_size(B, L, heads, C // heads)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib().wan_self_attn_fwd_ws(_ptr(out), _ptr(lse), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(k_lens), B, L, heads, C // heads, ld_q, ld_k, ld_v,
+                                    ld_o, scale, _ptr(ws), ws_bytes, _stream(q))
+    check("wan_self_attn_fwd_ws", st)
     return (out, lse) if return_lse else out
 
 

@@ -41,6 +41,7 @@
 #ifndef WANATTN_H_
 #define WANATTN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -142,6 +143,40 @@ wanStatus_t wan_self_attn_fwd(void* o, float* lse, const void* q,
                               int D, int64_t ld_q, int64_t ld_k, int64_t ld_v,
                               int64_t ld_o, float softmax_scale,
                               hipStream_t stream);
+
+/*
+ * wan_self_attn_workspace_size / wan_self_attn_fwd_ws: wan_self_attn_fwd with
+ * a caller-owned workspace, which lets the library even out the last round of
+ * work on the current device.
+ *
+ * Same passage and arithmetic as wan_self_attn_fwd. The call runs one work
+ * item (256 query rows of one (batch, head)) per compute unit at a time;
+ * when the items of the last round would leave at least half of the device
+ * idle, each of them is split into key ranges that run on the idle units,
+ * and a second kernel combines their partial results: for ranges s with
+ * running maxima m_s, sums l_s and unnormalised outputs O_s,
+ *   o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+ * the exact softmax over the union of the ranges (up to fp32 rounding), so o
+ * and lse match wan_self_attn_fwd to rounding.
+ *
+ * wan_self_attn_workspace_size returns the bytes of workspace a call with
+ * these sizes needs on the current device (0: no split, the workspace is not
+ * used and may be NULL; also 0 for sizes wan_self_attn_fwd would reject).
+ * workspace: device memory of at least that many bytes, 16-byte aligned,
+ * overlapping no other argument; its contents on entry do not matter and are
+ * left undefined. Calls that run at the same time need separate workspaces.
+ * Errors: as wan_self_attn_fwd, and WAN_ERROR_INVALID_VALUE for a workspace
+ * that is needed and NULL, misaligned, too small or overlapping a tensor.
+ */
+size_t wan_self_attn_workspace_size(int B, int L, int H, int D);
+
+wanStatus_t wan_self_attn_fwd_ws(void* o, float* lse, const void* q,
+                                 const void* k, const void* v,
+                                 const int32_t* k_lens, int B, int L, int H,
+                                 int D, int64_t ld_q, int64_t ld_k,
+                                 int64_t ld_v, int64_t ld_o,
+                                 float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * wan_cross_attn_fwd: cross-attention of video tokens to text tokens.

@@ -138,6 +138,35 @@ def test_self_attn_rejections(L):
     assert attn(L, Lt=1 << 20, **far) == NS
 
 
+def test_self_attn_workspace_rejections(L):
+    G = 1 << 28                          # fake tensors of 167 MB each stay apart
+    B, Lq, H = 1, 27280, 24              # 2568 work items: 8 in the last round of a 256-unit device
+    need = L.wan_self_attn_workspace_size(B, Lq, H, 128)
+    assert L.wan_self_attn_workspace_size(0, Lq, H, 128) == 0
+    assert L.wan_self_attn_workspace_size(B, Lq, H, 64) == 0
+    assert L.wan_self_attn_workspace_size(1, 1024, 1, 128) == 0     # too few key tiles to split
+
+    def ws(**kw):
+        a = dict(o=A, lse=None, q=A + G, k=A + 2 * G, v=A + 3 * G, kl=None, B=B, L=Lq, H=H,
+                 D=128, ws=A + 4 * G, wsb=need, scale=0.0)
+        a.update(kw)
+        return L.wan_self_attn_fwd_ws(a["o"], a["lse"], a["q"], a["k"], a["v"], a["kl"], a["B"],
+                                      a["L"], a["H"], a["D"], 0, 0, 0, 0, a["scale"], a["ws"],
+                                      a["wsb"], None)
+    assert ws(B=0, ws=None, wsb=0) == OK
+    assert ws(D=64) == NS
+    assert ws(q=None) == INV
+    assert ws(o=A + G) == INV                # o overlaps q
+    if need == 0:                            # no device to plan for: the workspace is unused
+        return
+    assert need == 8 * 32 * (256 * 128 + 2 * 256) * 4
+    assert ws(ws=None) == INV
+    assert ws(wsb=need - 16) == INV
+    assert ws(ws=A + 4 * G + 8) == INV       # misaligned
+    assert ws(ws=A + 2 * G) == INV           # overlaps k
+    assert ws(lse=A + 4 * G + 64, ws=A + 4 * G) == INV   # overlaps lse
+
+
 def test_cross_attn_rejections(L):
     def cross(**kw):
         a = dict(o=A, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, cl=None, B=1, Lq=64, Lk=32, H=2,

@@ -14,5 +14,10 @@ hipError_t launch_attn_fwd(const AttnArgs&, int, hipStream_t) { return hipErrorN
 hipError_t launch_linear(const LinearArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quant8(const Quant8Args&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attn8_fwd(const Attn8Args&, hipStream_t) { return hipErrorNotSupported; }
+// a 256-unit device, so that workspace sizes are those of the real one
+hipError_t device_cu_count(int* n) {
+  *n = 256;
+  return hipSuccess;
+}
 
 }  // namespace wan

@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 from attention_wan_qk_amd import ops, synth
-from attention_wan_qk_amd.workloads import WORKLOADS
+from attention_wan_qk_amd.workloads import BY_NAME, WORKLOADS
 from tests._parity import compare
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +134,73 @@ def test_self_attn_ragged(B, L, H):
     ref, rl = O.self_attention(qb, kb, vb, H, kl.numpy())
     compare(f"ragged {B}x{L}x{H}", synth.bf16_bits(o), ref)
     assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3
+
+
+@pytest.mark.parametrize("n_tiles", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_attn_every_key_tile_count(n_tiles):
+    """Self- and cross-attention over 1 to 8 key tiles of 64 (even and odd
+    counts take different last loop iterations), with a full and a ragged
+    last tile, on peaked logits (scale 4/sqrt(d)): a key tile counted twice
+    or skipped moves outputs by O(1) there, where diffuse logits would hide
+    it. All rows and lse against the oracle."""
+    H = 2
+    C = 128 * H
+    sc = 4.0 / math.sqrt(128)
+    for L in (64 * n_tiles, 64 * n_tiles - 5):
+        _announce(f"self/cross attn over {L} keys ({n_tiles} tiles)")
+        q, k, v = (_rand((1, L, C), s) for s in (21, 22, 23))
+        o, lse = ops.self_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), H, scale=sc, return_lse=True)
+        qc = _rand((1, 300, C), 24)
+        oc = ops.cross_attn_fwd(qc.to(DEV), k.to(DEV), v.to(DEV), H, scale=sc)
+        torch.cuda.synchronize()
+        qb, kb, vb = (synth.bf16_bits(t) for t in (q, k, v))
+        ref, rl = O.self_attention(qb, kb, vb, H, scale=sc)
+        st = compare(f"self {L} keys", synth.bf16_bits(o), ref)
+        assert st["rel_l2"] < 1e-2
+        assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3
+        refc, _ = O.cross_attention(synth.bf16_bits(qc), kb, vb, H, scale=sc)
+        st = compare(f"cross {L} keys", synth.bf16_bits(oc), refc)
+        assert st["rel_l2"] < 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_self_attn_key_split_of_the_last_round():
+    """The binding's workspace call splits the work items of the last round
+    into key ranges when they would leave half of the device idle (here 2
+    samples x 3 heads x 16 query tiles = 96 items of 64 key tiles on a
+    256-unit device, so each splits 2 ways) and merges the ranges; the second
+    sample's key length of 50 (one key tile) leaves one range of each of its
+    items empty.
+    All rows of every head and lse against the oracle, and against the
+    unsplit call (wan_self_attn_fwd) to rounding."""
+    from attention_wan_qk_amd import _lib
+    B, L, H = 2, 4096, 3
+    C = 128 * H
+    _announce("self_attn key split of the last round")
+    need = _lib.lib().wan_self_attn_workspace_size(B, L, H, 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    items = B * H * (L // 256)
+    if items % cus == 0 or 2 * (items % cus) > cus:
+        pytest.skip(f"no split on a device of {cus} units")
+    assert need > 0
+    q, k, v = (_rand((B, L, C), s) for s in (31, 32, 33))
+    kl = torch.tensor([L, 50], dtype=torch.int32)
+    qd, kd, vd, kld = q.to(DEV), k.to(DEV), v.to(DEV), kl.to(DEV)   # held: pointers go to C
+    o, lse = ops.self_attn_fwd(qd, kd, vd, H, k_lens=kld, return_lse=True)
+    o_plain = torch.empty_like(o)
+    lse_plain = torch.empty_like(lse)
+    st = _lib.lib().wan_self_attn_fwd(o_plain.data_ptr(), lse_plain.data_ptr(), qd.data_ptr(),
+                                      kd.data_ptr(), vd.data_ptr(), kld.data_ptr(), B, L, H, 128,
+                                      0, 0, 0, 0, 0.0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    qb, kb, vb = (synth.bf16_bits(t) for t in (q, k, v))
+    ref, rl = O.self_attention(qb, kb, vb, H, kl.numpy())
+    compare("split tail", synth.bf16_bits(o), ref)
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3
+    d = (o.float() - o_plain.float()).abs().max().item()
+    assert d <= 2.0 ** -7 * max(1.0, o_plain.float().abs().max().item())
+    assert torch.allclose(lse, lse_plain, rtol=0, atol=1e-5)
 
 
 @pytest.mark.parametrize("Lk", [1, 7, 32, 511, 512, 513])
@@ -385,6 +452,32 @@ def test_determinism_and_side_stream():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.timeout(600)
+def test_determinism_at_full_size():
+    """Two launches of the benchmark's self-attention (2 x 75,600 tokens x 40
+    heads), of the same shape's chunk-causal call (3-frame chunks) and of the
+    cross-attention are bitwise equal, lse included: no atomics, and the lazy
+    rescale, the LDS-direct loads and the fence-free barriers take the same
+    path on every run."""
+    w = BY_NAME["a14b-720p-cfg"]
+    _announce("determinism at full size (a14b-720p-cfg)")
+    q, k, v = (synth.tensor(w, t, DEV) for t in ("q", "k", "v"))
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    runs = []
+    for _ in range(2):
+        o, lse = ops.self_attn_fwd(q, k, v, w.heads, return_lse=True)
+        chunk = 3 * w.grid[1] * w.grid[2]
+        oc, lc = ops.chunk_causal_attn_fwd(q, k, v, w.heads, 0, chunk, return_lse=True)
+        tq, tk, tv = (synth.tensor(w, t, DEV) for t in ("cross_q", "text_k", "text_v"))
+        ox = ops.cross_attn_fwd(tq, tk, tv, w.heads)
+        torch.cuda.synchronize()
+        runs.append([bits(t).clone() for t in (o, lse, oc, lc, ox)])
+        del o, lse, oc, lc, ox, tq, tk, tv
+    for a, b, name in zip(runs[0], runs[1], ("self o", "self lse", "chunk o", "chunk lse",
+                                             "cross o")):
+        assert torch.equal(a, b), f"{name} differs between two launches"
 
 
 @pytest.mark.timeout(600)
