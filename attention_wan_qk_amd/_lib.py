@@ -33,6 +33,8 @@ SIGNATURES = {
     "wan_self_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "wan_self_attn_fwd_ws": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _L,
                                   _F, _P, ctypes.c_size_t, _P]),
+    "wan_self_attn_fwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _L,
+                                       _F, _P]),
     "wan_cross_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _L, _F,
                                 _P]),
     "wan_chunk_causal_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,

@@ -543,8 +543,35 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_device_mutex;
 int g_cus[kMaxDevices];                 // 0: not looked up yet
+void* g_scratch[kMaxDevices];           // device address of `scratch`; nullptr: not looked up yet
+constexpr uint64_t kScratchBytes = 256 * kAttnPartFloats * 4;
 
 }  // namespace
+
+// Key-split partial results of the allocation-free entry point: one partial
+// per compute unit of a 256-unit device (34 MB, held by each GPU the library
+// runs on until the process ends).
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t device_scratch(void** p, uint64_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_device_mutex);
+  if (g_scratch[dev] == nullptr) {
+    // In host code `scratch` is only a stand-in: the device address of this
+    // device's copy comes from the runtime, looked up once per device with
+    // that device current.
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *p = g_scratch[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t device_cu_count(int* n) {
   int dev = 0;

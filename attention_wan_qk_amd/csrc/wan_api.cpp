@@ -290,6 +290,31 @@ wanStatus_t wan_self_attn_fwd_ws(void* o, float* lse, const void* q, const void*
                    part, split, stream);
 }
 
+wanStatus_t wan_self_attn_fwd_noalloc(void* o, float* lse, const void* q, const void* k,
+                                      const void* v, const int32_t* k_lens, int B, int L, int H,
+                                      int D, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                                      int64_t ld_o, float softmax_scale, hipStream_t stream) {
+  if (B < 0 || L < 0) return WAN_ERROR_INVALID_VALUE;
+  if ((int64_t)B * L == 0) {
+    if (H < 1 || D < 1) return WAN_ERROR_INVALID_VALUE;
+    return D == kHeadDim ? WAN_SUCCESS : WAN_ERROR_NOT_SUPPORTED;
+  }
+  wanStatus_t st = check_attn(o, lse, q, k, v, B, L, L, H, D, ld_q, ld_k, ld_v, ld_o,
+                              softmax_scale);
+  if (st != WAN_SUCCESS) return st;
+  const wan::AttnSplit split = self_attn_split(B, L, H);
+  float* part = nullptr;
+  if (split.bytes > 0) {
+    void* p = nullptr;
+    uint64_t bytes = 0;
+    if (wan::device_scratch(&p, &bytes) != hipSuccess) return WAN_ERROR_LAUNCH;
+    if (split.bytes > bytes) return WAN_ERROR_NOT_SUPPORTED;
+    part = static_cast<float*>(p);
+  }
+  return self_attn(o, lse, q, k, v, k_lens, B, L, H, ld_q, ld_k, ld_v, ld_o, softmax_scale,
+                   part, split, stream);
+}
+
 wanStatus_t wan_cross_attn_fwd(void* o, const void* q, const void* k, const void* v,
                                const int32_t* context_lens, int B, int Lq, int Lk, int H, int D,
                                int64_t ld_q, int64_t ld_kv, int64_t ld_o, float softmax_scale,

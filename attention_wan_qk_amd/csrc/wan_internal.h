@@ -90,6 +90,9 @@ inline AttnSplit plan_self_attn_split(int64_t items, int n_tiles, int cus) {
 
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int* n);
+// Device address and size of the library's static scratch array on the
+// current device (looked up once per device).
+hipError_t device_scratch(void** p, uint64_t* bytes);
 
 struct LinearArgs {
   void* y;

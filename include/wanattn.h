@@ -179,6 +179,28 @@ wanStatus_t wan_self_attn_fwd_ws(void* o, float* lse, const void* q,
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * wan_self_attn_fwd_noalloc: wan_self_attn_fwd_ws without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, arithmetic and errors as wan_self_attn_fwd, same results
+ * as wan_self_attn_fwd_ws. The key-split partial results go to a static
+ * device array of the library (34 MB, one per device, kept until the process
+ * ends; its address is looked up on the first call on each device). The call
+ * allocates and frees nothing. Every call on one device shares that array:
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be serialised by the caller. A split needing more than the array
+ * (a device of more than 256 compute units) returns WAN_ERROR_NOT_SUPPORTED;
+ * a failed address lookup returns WAN_ERROR_LAUNCH.
+ */
+wanStatus_t wan_self_attn_fwd_noalloc(void* o, float* lse, const void* q,
+                                      const void* k, const void* v,
+                                      const int32_t* k_lens, int B, int L,
+                                      int H, int D, int64_t ld_q, int64_t ld_k,
+                                      int64_t ld_v, int64_t ld_o,
+                                      float softmax_scale, hipStream_t stream);
+
+/*
  * wan_cross_attn_fwd: cross-attention of video tokens to text tokens.
  *
  * Passage: cross_attn(norm3(x), context, context_lens) in the WanAttentionBlock

@@ -167,6 +167,28 @@ def test_self_attn_workspace_rejections(L):
     assert ws(lse=A + 4 * G + 64, ws=A + 4 * G) == INV   # overlaps lse
 
 
+def test_self_attn_noalloc_rejections(L):
+    def na(**kw):
+        a = dict(o=A, lse=None, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, kl=None, B=1, L=100, H=2,
+                 D=128, lq=0, lk=0, lv=0, lo=0, scale=0.0)
+        a.update(kw)
+        return L.wan_self_attn_fwd_noalloc(a["o"], a["lse"], a["q"], a["k"], a["v"], a["kl"],
+                                           a["B"], a["L"], a["H"], a["D"], a["lq"], a["lk"],
+                                           a["lv"], a["lo"], a["scale"], None)
+    assert na(B=0) == OK
+    assert na(D=64) == NS
+    assert na(q=None) == INV
+    assert na(o=A + 8) == INV                # misaligned
+    assert na(o=A + MB) == INV               # o overlaps q
+    assert na(lo=100) == INV
+    assert na(scale=float("nan")) == INV
+    if os.environ.get("WANATTN_TEST_LIB"):
+        # host-only build: a call that needs the scratch array cannot look it up
+        # there (its stand-in reports no device) and must say so, not launch
+        G = 1 << 28
+        assert na(q=A + G, k=A + 2 * G, v=A + 3 * G, L=27280, H=24) == 3
+
+
 def test_cross_attn_rejections(L):
     def cross(**kw):
         a = dict(o=A, q=A + MB, k=A + 2 * MB, v=A + 3 * MB, cl=None, B=1, Lq=64, Lk=32, H=2,

@@ -14,6 +14,8 @@ hipError_t launch_attn_fwd(const AttnArgs&, int, hipStream_t) { return hipErrorN
 hipError_t launch_linear(const LinearArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quant8(const Quant8Args&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attn8_fwd(const Attn8Args&, hipStream_t) { return hipErrorNotSupported; }
+// no device: the allocation-free call cannot look up its scratch array
+hipError_t device_scratch(void**, uint64_t*) { return hipErrorNotSupported; }
 // a 256-unit device, so that workspace sizes are those of the real one
 hipError_t device_cu_count(int* n) {
   *n = 256;
