@@ -383,6 +383,35 @@ def test_cross_attn_many_tiles_mixed_lengths():
     compare("cross 320 tiles", synth.bf16_bits(o), ref)
 
 
+def test_cross_attn_staged_items_ragged_strided():
+    """Persistent cross-attention workgroups taking several items (2 x 8
+    heads x 20 query tiles = 320 > 256): after its first item a workgroup
+    reads Q rows staged in LDS during the previous item and stores outputs
+    as whole rows through LDS. Ragged last tile (Lq = 20 x 256 - 37),
+    context lengths 0 and 300, q and o rows with a stride of C + 64: the
+    padding columns and the rows after the output must stay untouched."""
+    _announce("cross_attn staged items, ragged Lq, strided q/o")
+    B, Lq, Lk, H = 2, 20 * 256 - 37, 512, 8
+    C = 128 * H
+    ld = C + 64
+    qb = _rand((B, Lq, ld), 44)
+    k, v = _rand((B, Lk, C), 45), _rand((B, Lk, C), 46)
+    cl = torch.tensor([0, 300], dtype=torch.int32)
+    sentinel = torch.tensor(3.0, dtype=torch.bfloat16)
+    obuf = torch.full((B * Lq + 3, ld), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = obuf[:B * Lq].view(B, Lq, ld)[:, :, :C]
+    o = ops.cross_attn_fwd(qb.to(DEV)[:, :, :C], k.to(DEV), v.to(DEV), H, context_lens=cl.to(DEV),
+                           out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    assert torch.all(o[0] == 0)
+    assert torch.all(obuf[:B * Lq, C:].cpu() == sentinel)
+    assert torch.all(obuf[B * Lq:].cpu() == sentinel)
+    ref, _ = O.cross_attention(synth.bf16_bits(qb[:, :, :C].contiguous()), synth.bf16_bits(k),
+                               synth.bf16_bits(v), H, cl.numpy())
+    compare("cross staged ragged strided", synth.bf16_bits(o.contiguous()), ref)
+
+
 @pytest.mark.parametrize("pattern", ["rising", "falling", "spike", "sawtooth"])
 def test_self_attn_running_max_paths(pattern):
     """Logits whose tile maxima follow a set pattern across the 12 key tiles
