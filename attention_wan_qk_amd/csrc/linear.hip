@@ -193,27 +193,45 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
   }
 
   // Epilogue: acc[i][j][4 g + e] is y[m][n + e] for token m = tile row
-  // 128 wm + 32 j + r32 and feature n = 64 wn + 32 i + 8 g + 4 hf.
-  uint16_t* const y = static_cast<uint16_t*>(a.y);
+  // 128 wm + 32 j + r32 and feature n = 64 wn + 32 i + 8 g + 4 hf. Each wave
+  // stages its 128 x 64 block (bias added, bf16) in the LDS array of its
+  // feature quarter (the K loop ended with a barrier, so every stage is free)
+  // and stores it back as whole 128-byte row segments: written from the
+  // registers directly, each store covered 32 rows with 16 bytes, and the
+  // partial lines cost about three times the output's bytes in HBM writes.
+  // Row r of a quarter keeps 16-byte chunk c at c ^ (r % 8).
+  lds_char* const stage = wn == 0 ? W0 : wn == 1 ? W1 : wn == 2 ? X0 : X1;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * 64 + i * 32 + g * 8 + hf * 4;
-      if (n >= a.N) continue;
+      const int nq = i * 32 + g * 8 + hf * 4;   // feature inside the quarter
+      const int n = n0 + wn * 64 + nq;
       f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (a.bias) b = *reinterpret_cast<const f32x4*>(a.bias + n);
+      if (a.bias && n < a.N) b = *reinterpret_cast<const f32x4*>(a.bias + n);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int m = m0 + wm * 128 + j * 32 + r32;
-        if (m >= a.M) continue;
+        const int r = wm * 128 + j * 32 + r32;
         f32x4 v = {acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1],
                    acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]};
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 o = __builtin_convertvector(v, bf16x4);
-        *reinterpret_cast<u32x2*>(y + (int64_t)m * a.ld_y + n) = __builtin_bit_cast(u32x2, o);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+            stage + r * kRowBytes + (((4 * i + g) ^ (r & 7)) << 4) + 8 * hf) = __builtin_bit_cast(u32x2, o);
       }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's block is staged
+  uint16_t* const y = static_cast<uint16_t*>(a.y);
+  const int c = lane & 7;
+  const int n = n0 + wn * 64 + c * 8;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = wm * 128 + k * 8 + (lane >> 3);
+    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        stage + r * kRowBytes + ((c ^ (r & 7)) << 4));
+    const int m = m0 + r;
+    if (m < a.M && n < a.N) *reinterpret_cast<u32x4*>(y + (int64_t)m * a.ld_y + n) = v;
   }
 }
 
