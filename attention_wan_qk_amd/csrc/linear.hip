@@ -4,26 +4,29 @@
 //
 // Both operands are read along K (x rows and W rows are K-contiguous), so the
 // product is computed transposed, Y^T tile = W_tile X_tile^T, on
-// v_mfma_f32_32x32x16_bf16 with W as the A operand and x as the B operand.
-// In the accumulator each lane then owns one token row and runs of 4
-// consecutive output features, which it stores as one 8-byte bf16 vector.
+// v_mfma_f32_16x16x32_bf16 with W as the A operand and x as the B operand
+// (in a pure loop this MFMA sustains ~12% more than v_mfma_f32_32x32x16_bf16
+// on gfx950). In the accumulator each lane then owns one token row and runs
+// of 4 consecutive output features.
 //
 // Work layout:
 //  * One workgroup computes a 256 (tokens) x 256 (features) tile with 8
-//    wavefronts (2 along tokens x 4 along features, 128 x 64 each: 8
-//    accumulator tiles of 32 x 32 per wave, two waves per SIMD).
+//    wavefronts (2 along tokens x 4 along features, 128 x 64 each: 32
+//    accumulator tiles of 16 x 16 per wave, two waves per SIMD).
 //  * K advances in steps of 64 through a double-buffered LDS stage (x and W
 //    tiles, 32 KiB each). The tiles of step k+1 are moved by buffer loads
 //    whose destination is the LDS (no register staging), issued with the
-//    MFMAs of the first two of step k's four 16-deep k-steps into the other
+//    MFMAs of step k's two 32-deep k-steps into the other
 //    buffer; each wave waits for its own loads before the step's barrier,
 //    which publishes them: one barrier per step. The two buffers are reached through restrict pointers of an
 //    inlined step function, so the compiler can tell that the loads in
 //    flight do not write what the step's LDS reads read, and places no wait
 //    before those reads.
 //  * Each 16-byte chunk c of tile row r is stored at chunk c ^ ((r / 2) % 8),
-//    so the 16 rows read together at one logical chunk by half a wave fall
-//    into 16 different 16-byte bank groups.
+//    so the 16 rows read together at one logical chunk by a quarter of a
+//    wave fall into 16 different 16-byte bank groups.
+//  * The finished 256 x 256 tile goes out through the LDS (see the epilogue):
+//    whole 128-byte row segments per store.
 //  * Rows past M or N fall outside the buffer resource and read as zero;
 //    chunks past K get an offset outside it and read as zero too.
 //  * Tiles are walked in bands of 4 token tiles (all feature tiles of a band
@@ -44,7 +47,7 @@ constexpr int kThreads = 512;
 constexpr int kRowBytes = kBK * 2;       // 128
 constexpr int kTileBytes = kBM * kRowBytes;  // 32 KiB (x and W tiles are the same size)
 constexpr int kLoads = kTileBytes / 16 / kThreads;  // 1 KiB loads per wave per tile: 4
-constexpr int kLoadGroups = 2;          // the next stage's loads go out with the first 2 k-steps
+constexpr int kLoadGroups = 2;          // the next stage's loads go out with the 2 k-steps
 constexpr int kGroupM = 4;               // token tiles per band
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -68,7 +71,7 @@ __device__ __forceinline__ void k_step(int kt, bool more, const lds_char* __rest
                                        const lds_char* __restrict__ wc, lds_char* __restrict__ xn,
                                        lds_char* __restrict__ wn, Dma& dma, Mma& mma) {
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
+  for (int kk = 0; kk < kBK / 32; ++kk) {
     if (more && kk < kLoadGroups) dma(kt + 1, xn, wn, kk);
     mma(xc, wc, kk);
     __builtin_amdgcn_sched_barrier(0);   // keep each group of loads with its k-step
@@ -90,8 +93,6 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
   const int wave = tid >> 6;
   const int wm = wave & 1;       // token half: rows 128 wm ..
   const int wn = wave >> 1;      // feature quarter: 64 wn ..
-  const int r32 = lane & 31;
-  const int hf = lane >> 5;
 
   const int nM = (a.M + kBM - 1) / kBM;
   const int nN = (a.N + kBN - 1) / kBN;
@@ -142,40 +143,42 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // Fragment read offsets: lane reads row (base + r32), logical chunk
-  // 2 kk + hf of k-step kk; the 32-row sub-tiles are immediate offsets.
-  const int sw = (r32 >> 1) & 7;
+  // Fragment read offsets (v_mfma_f32_16x16x32_bf16): lane l reads row
+  // (base + l % 16), logical chunk 4 kk + l / 16 of k-step kk (32 of the
+  // stage's K values); the 16-row sub-tiles are immediate offsets, and the
+  // swizzle of a row depends only on its index within 16.
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int sw = (r16 >> 1) & 7;
   const int nK = (a.K + kBK - 1) / kBK;
-  const int xa = (wm * 128 + r32) * kRowBytes;
-  const int wa = (wn * 64 + r32) * kRowBytes;
-  int ch[4];
+  const int xa = (wm * 128 + r16) * kRowBytes;
+  const int wa = (wn * 64 + r16) * kRowBytes;
+  int ch[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) ch[kk] = ((2 * kk + hf) ^ sw) << 4;
+  for (int kk = 0; kk < 2; ++kk) ch[kk] = ((4 * kk + q4) ^ sw) << 4;
 
-  f32x16 acc[2][4];
+  // acc[f][t][e]: feature 16 f + 4 q4 + e, token 16 t + r16 of the wave's block
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
-  // MFMAs of k-step kk (16 of the stage's 64 K values).
+  // MFMAs of k-step kk (32 of the stage's 64 K values).
   auto mma = [&](const lds_char* __restrict__ xc, const lds_char* __restrict__ wc, int kk) {
     const lds_char* wb = wc + wa;
     const lds_char* xb = xc + xa;
-    {
-      bf16x8 wf[2], xf[4];
+    bf16x8 wf[4], xf[8];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wf[i] = lds_read16(wb + ch[kk] + i * 32 * kRowBytes);
+    for (int i = 0; i < 4; ++i) wf[i] = lds_read16(wb + ch[kk] + i * 16 * kRowBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xf[j] = lds_read16(xb + ch[kk] + j * 32 * kRowBytes);
+    for (int j = 0; j < 8; ++j) xf[j] = lds_read16(xb + ch[kk] + j * 16 * kRowBytes);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
   };
   dma(0, X0, W0, -1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
     }
   }
 
-  // Epilogue: acc[i][j][4 g + e] is y[m][n + e] for token m = tile row
-  // 128 wm + 32 j + r32 and feature n = 64 wn + 32 i + 8 g + 4 hf. Each wave
+  // Epilogue: acc[i][j][e] is y[m][n + e] for token m = tile row
+  // 128 wm + 16 j + r16 and feature n = 64 wn + 16 i + 4 q4. Each wave
   // stages its 128 x 64 block (bias added, bf16) in the LDS array of its
   // feature quarter (the K loop ended with a barrier, so every stage is free)
   // and stores it back as whole 128-byte row segments: written from the
@@ -202,23 +205,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
   // Row r of a quarter keeps 16-byte chunk c at c ^ (r % 8).
   lds_char* const stage = wn == 0 ? W0 : wn == 1 ? W1 : wn == 2 ? X0 : X1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    const int nq = i * 16 + q4 * 4;   // feature inside the quarter
+    const int n = n0 + wn * 64 + nq;
+    f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.bias && n < a.N) b = *reinterpret_cast<const f32x4*>(a.bias + n);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int nq = i * 32 + g * 8 + hf * 4;   // feature inside the quarter
-      const int n = n0 + wn * 64 + nq;
-      f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (a.bias && n < a.N) b = *reinterpret_cast<const f32x4*>(a.bias + n);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 128 + j * 32 + r32;
-        f32x4 v = {acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1],
-                   acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]};
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 o = __builtin_convertvector(v, bf16x4);
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-            stage + r * kRowBytes + (((4 * i + g) ^ (r & 7)) << 4) + 8 * hf) = __builtin_bit_cast(u32x2, o);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int r = wm * 128 + j * 16 + r16;
+      f32x4 v = acc[i][j] + b;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 o = __builtin_convertvector(v, bf16x4);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + r * kRowBytes + (((nq >> 3) ^ (r & 7)) << 4) + 8 * ((nq >> 2) & 1)) =
+          __builtin_bit_cast(u32x2, o);
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's block is staged
