@@ -42,6 +42,11 @@
 //    global chunk that belongs there.
 //  * Workgroup ids are remapped so that each XCD works through consecutive
 //    query tiles of the same (batch, head) and shares its K/V in its L2.
+//  * The output rows leave through LDS: each wave stages its normalised
+//    32 x 128 block and stores whole 256-byte row segments, 4 rows per store
+//    instruction (the accumulator layout alone would give 16-byte pieces of
+//    32 rows per instruction), which matters for the cross-attention items of
+//    only a few key tiles.
 //  * With a workspace (self-attention), the work items of the last, partly
 //    filled round of the chip are split into key ranges run by otherwise idle
 //    CUs; each range leaves its unnormalised output, running max and sum, and
@@ -444,9 +449,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         pp[kBM * kHD + prow] = m_used;
         pp[kBM * kHD + kBM + prow] = lsum;
       }
-    } else if (qrow < a.Lq) {
+    } else {
+      // Normalised bf16 rows go through LDS (every K/V slot is free after the
+      // loop's last barrier): each wave stages its own 32 x 128 block, 16-byte
+      // chunk c of row r at chunk c ^ (r % 16), then stores whole 256-byte row
+      // segments, 4 rows per instruction, instead of 16-byte pieces of 32 rows.
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-      uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)b * a.Lq + qrow) * a.ld_o + h * kHD;
+      char* const st = smem + wave * (32 * kRowBytes);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -455,10 +464,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                      oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 y = __builtin_convertvector(x, bf16x4);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hf) =
+          *reinterpret_cast<u32x2*>(st + r32 * kRowBytes + (((4 * db + a4) ^ (r32 & 15)) << 4) + 8 * hf) =
               __builtin_bit_cast(u32x2, y);
         }
-      if (a.lse && hf == 0) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
+      const int rq = lane >> 4, ch = lane & 15;
+      uint16_t* const obase = static_cast<uint16_t*>(a.o) + h * kHD + 8 * ch;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + rq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * kRowBytes + ((ch ^ (r & 15)) << 4));
+        const int row = qt * kBM + wave * 32 + r;
+        if (row < a.Lq) *reinterpret_cast<u32x4*>(obase + ((int64_t)b * a.Lq + row) * a.ld_o) = v;
+      }
+      if (qrow < a.Lq && a.lse && hf == 0) {
         a.lse[((int64_t)b * a.H + h) * a.Lq + qrow] =
             lsum > 0.f ? m_used * 0.6931471805599453f + logf(lsum) : -INFINITY;
       }
