@@ -14,11 +14,14 @@
 //    wavefronts (2 along tokens x 4 along features, 128 x 64 each: 32
 //    accumulator tiles of 16 x 16 per wave, two waves per SIMD).
 //  * K advances in steps of 64 through a double-buffered LDS stage (x and W
-//    tiles, 32 KiB each). The tiles of step k+1 are moved by buffer loads
-//    whose destination is the LDS (no register staging), issued with the
-//    MFMAs of step k's two 32-deep k-steps into the other
-//    buffer; each wave waits for its own loads before the step's barrier,
-//    which publishes them: one barrier per step. The two buffers are reached through restrict pointers of an
+//    tiles, 32 KiB each). The tiles of step k+1 are moved into the other
+//    buffer by buffer loads whose destination is the LDS (no register
+//    staging); each wave waits for its own loads before the step's barrier,
+//    which publishes them: one barrier per step. A wave stalls while its
+//    loads queue for the compute unit's load path (~50 bytes per cycle), so
+//    waves 0-3 issue theirs before the step's first 32-deep k-step and waves
+//    4-7 before its second: the two waves of each SIMD stall at different
+//    times and the MFMA pipe keeps running on the other one. The two buffers are reached through restrict pointers of an
 //    inlined step function, so the compiler can tell that the loads in
 //    flight do not write what the step's LDS reads read, and places no wait
 //    before those reads.
@@ -47,7 +50,6 @@ constexpr int kThreads = 512;
 constexpr int kRowBytes = kBK * 2;       // 128
 constexpr int kTileBytes = kBM * kRowBytes;  // 32 KiB (x and W tiles are the same size)
 constexpr int kLoads = kTileBytes / 16 / kThreads;  // 1 KiB loads per wave per tile: 4
-constexpr int kLoadGroups = 2;          // the next stage's loads go out with the 2 k-steps
 constexpr int kGroupM = 4;               // token tiles per band
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -63,18 +65,19 @@ __device__ __forceinline__ bf16x8 lds_read16(const lds_char* p) {
 }
 
 // One K step: the loads of the next stage go to (xn, wn) while the MFMAs read
-// the current stage (xc, wc). The four LDS pointers are restrict parameters of
+// the current stage (xc, wc); this wave issues them before k-step lg. The four
+// LDS pointers are restrict parameters of
 // an inlined function, so the compiler knows the loads in flight do not write
 // what the reads below read and needs no wait before them.
 template <typename Dma, typename Mma>
-__device__ __forceinline__ void k_step(int kt, bool more, const lds_char* __restrict__ xc,
+__device__ __forceinline__ void k_step(int kt, bool more, int lg, const lds_char* __restrict__ xc,
                                        const lds_char* __restrict__ wc, lds_char* __restrict__ xn,
                                        lds_char* __restrict__ wn, Dma& dma, Mma& mma) {
 #pragma unroll
   for (int kk = 0; kk < kBK / 32; ++kk) {
-    if (more && kk < kLoadGroups) dma(kt + 1, xn, wn, kk);
+    if (more && kk == lg) dma(kt + 1, xn, wn);
     mma(xc, wc, kk);
-    __builtin_amdgcn_sched_barrier(0);   // keep each group of loads with its k-step
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads with their k-step
   }
 }
 
@@ -123,13 +126,10 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
     vo_x[i] = r * row_x + lch[i] * 16;
     vo_w[i] = r * row_w + lch[i] * 16;
   }
-  // group g < kLoadGroups issues loads i with i / (kLoads / kLoadGroups) == g;
-  // group -1 issues all of them.
-  auto dma = [&](int kt, lds_char* __restrict__ xd, lds_char* __restrict__ wd, int group) {
+  auto dma = [&](int kt, lds_char* __restrict__ xd, lds_char* __restrict__ wd) {
     const uint32_t so = (uint32_t)kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      if (group >= 0 && i / (kLoads / kLoadGroups) != group) continue;
       const uint32_t oor = (kt * kBK + (int)lch[i] * 8 >= a.K) ? kOutOfRange : 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xd + (4 * wave + i) * 1024), 16,
                                                vo_x[i] + oor, so, 0, 0);
@@ -180,16 +180,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
       for (int j = 0; j < 8; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
   };
-  dma(0, X0, W0, -1);
+  dma(0, X0, W0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   barrier();
 
+  // Waves 0-3 issue a stage's loads before its first k-step, waves 4-7 before
+  // its second: the two waves of a SIMD stall on load issue at different
+  // times, and the other one keeps the MFMA pipe busy meanwhile.
+  const int lg = __builtin_amdgcn_readfirstlane(wave) >> 2;
   for (int kt = 0; kt < nK; kt += 2) {
-    k_step(kt, kt + 1 < nK, X0, W0, X1, W1, dma, mma);
+    k_step(kt, kt + 1 < nK, lg, X0, W0, X1, W1, dma, mma);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's tile loads have landed
     barrier();
     if (kt + 1 < nK) {
-      k_step(kt + 1, kt + 2 < nK, X1, W1, X0, W0, dma, mma);
+      k_step(kt + 1, kt + 2 < nK, lg, X1, W1, X0, W0, dma, mma);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       barrier();
     }
