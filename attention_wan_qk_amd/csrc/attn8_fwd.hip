@@ -278,20 +278,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(Attn8Args a) {
     auto exps = [&]() __attribute__((always_inline)) {
       const float cc = -(kBias * mult) - m_used;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sg[i] = 0.f;
-#pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + e], mult, cc));
-          sg[e] += p[e];
+          // each partial sum starts at its first weight (no addition to 0)
+          sg[e] = q4 == 0 ? p[e] : sg[e] + p[e];
         }
         const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         pq[q4] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
       }
     };
-    bool exact = __any(m_used == -INFINITY);
+    // The range's first tile forms the row maxima. On a later tile a row whose
+    // maximum is still -inf would get weights of inf or NaN, which the sum
+    // check below sends through the exact path as well.
+    bool exact = jj == 0;
     if (!exact) {
       exps();
       const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));

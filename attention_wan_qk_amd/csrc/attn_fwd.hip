@@ -332,20 +332,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       auto exps = [&]() __attribute__((always_inline)) {
         const float neg_m = -m_used;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sg[i] = 0.f;
-#pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             p[e] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, neg_m));
-            sg[e & 3] += p[e];
+            // each partial sum starts at its first weight (no addition to 0)
+            if (kc == 0 && e < 4) sg[e] = p[e];
+            else sg[e & 3] += p[e];
           }
           f32x8 pv = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
           pf[kc] = __builtin_convertvector(pv, bf16x8);
         }
       };
-      bool exact = __any(m_used == -INFINITY);
+      // The range's first tile forms the row maxima. On a later tile a row whose
+      // maximum is still -inf would get weights of inf or NaN, which the sum
+      // check below sends through the exact path as well.
+      bool exact = jj == 0;
       if (!exact) {
         exps();
         const float big = fmaxf(fmaxf(sg[0], sg[1]), fmaxf(sg[2], sg[3]));
