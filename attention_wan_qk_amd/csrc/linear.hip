@@ -18,7 +18,7 @@
 //    buffer by buffer loads whose destination is the LDS (no register
 //    staging); each wave waits for its own loads before the step's barrier,
 //    which publishes them: one barrier per step. A wave stalls while its
-//    loads queue for the compute unit's load path (~50 bytes per cycle), so
+//    loads queue for the compute unit's load path (~64 bytes per cycle), so
 //    waves 0-3 issue theirs before the step's first 32-deep k-step and waves
 //    4-7 before its second: the two waves of each SIMD stall at different
 //    times and the MFMA pipe keeps running on the other one. The two buffers are reached through restrict pointers of an
