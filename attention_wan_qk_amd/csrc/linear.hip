@@ -21,10 +21,10 @@
 //    loads queue for the compute unit's load path (~64 bytes per cycle), so
 //    waves 0-3 issue theirs before the step's first 32-deep k-step and waves
 //    4-7 before its second: the two waves of each SIMD stall at different
-//    times and the MFMA pipe keeps running on the other one. The two buffers are reached through restrict pointers of an
-//    inlined step function, so the compiler can tell that the loads in
-//    flight do not write what the step's LDS reads read, and places no wait
-//    before those reads.
+//    times and the MFMA pipe keeps running on the other one. The two
+//    buffers are reached through restrict pointers of an inlined step
+//    function, so the compiler can tell that the loads in flight do not write
+//    what the step's LDS reads read, and places no wait before those reads.
 //  * Each 16-byte chunk c of tile row r is stored at chunk c ^ ((r / 2) % 8),
 //    so the 16 rows read together at one logical chunk by a quarter of a
 //    wave fall into 16 different 16-byte bank groups.
