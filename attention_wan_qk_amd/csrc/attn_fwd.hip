@@ -33,9 +33,12 @@
 //    conversion.
 //  * K/V tiles are double-buffered in LDS and moved by buffer loads whose
 //    destination is the LDS (no register staging), issued at the start of a
-//    softmax phase (which reads no LDS) and awaited at its end: group 1
-//    loads the next K tile, group 0 the next V tile, so neither group's
-//    phase carries all the load issue. Rows past k_len fall outside the
+//    softmax phase (which reads no LDS): group 1 loads the next K tile and
+//    awaits it at the end of its following GEMM phase (the tile is only
+//    needed one interval later), group 0 the next V tile, awaited at the end
+//    of the softmax phase. The four slots are separate LDS arrays, so the
+//    compiler places no wait for a load in flight before the reads of
+//    another slot. Rows past k_len fall outside the
 //    buffer resource and read as zero. Each 16-byte chunk of a row is
 //    XOR-swizzled so the MFMA operand reads are bank-conflict free; a load
 //    writes 16 bytes per lane at base + 16 lane, so each lane fetches the
@@ -126,9 +129,11 @@ __device__ __forceinline__ int v_phys(int r, int ch) { return ch ^ ((r & 3) << 2
 // profiles), 2 chunk-causal self-attention (per-row key limit, see below).
 template <int kKind>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
-  char* const Ks = smem;                    // K tiles, slots 0 and 1
-  char* const Vs = smem + 2 * kTileBytes;   // V tiles, slots 0 and 1
+  // K and V tiles, slots 0 and 1, each an array of its own: the compiler then
+  // knows that a tile load in flight into one slot does not write what the
+  // LDS reads of another slot read, and places no wait before those reads.
+  __shared__ __attribute__((aligned(1024))) char k_slot0[kTileBytes], k_slot1[kTileBytes],
+      v_slot0[kTileBytes], v_slot1[kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,21 +204,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       vo_k[i] = r * row_k + (k_phys(r, p) << 4);  // k_phys is an involution
       vo_v[i] = r * row_v + (v_phys(r, p) << 4);
     }
-    auto dma_k = [&](int t, int slot) {
+    auto dma_k = [&](int t, auto slotc) {
+      char* const dst = decltype(slotc)::value ? k_slot1 : k_slot0;
       const uint32_t sk = (uint32_t)(t0 + t) * kBN * row_k;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (lds_void*)(Ks + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
-            vo_k[i], sk, 0, 0);
+            rk, (lds_void*)(dst + ((wave & 3) * kLoadsPerWave + i) * 1024), 16, vo_k[i], sk, 0, 0);
     };
-    auto dma_v = [&](int t, int slot) {
+    auto dma_v = [&](int t, auto slotc) {
+      char* const dst = decltype(slotc)::value ? v_slot1 : v_slot0;
       const uint32_t sv = (uint32_t)(t0 + t) * kBN * row_v;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (lds_void*)(Vs + slot * kTileBytes + ((wave & 3) * kLoadsPerWave + i) * 1024), 16,
-            vo_v[i], sv, 0, 0);
+            rv, (lds_void*)(dst + ((wave & 3) * kLoadsPerWave + i) * 1024), 16, vo_v[i], sv, 0, 0);
     };
     // Q fragment: B operand of S^T = K Q^T, lane holds Q[row][16c + 8hf .. +8].
     const int qrow = qt * kBM + wave * 32 + r32;
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
     }
 
-    if (nT > 0 && group == 0) dma_k(0, 0);
+    if (nT > 0 && group == 0) dma_k(0, Int<0>{});
     __builtin_amdgcn_s_waitcnt(0);   // Q and K tile 0 have landed
     __syncthreads();
 
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     auto gemm = [&](auto ksc, int jj) {
       constexpr int KS = decltype(ksc)::value;
       if (jj >= 1 && jj <= nT) {
-        const char* Vt = Vs + (1 - KS) * kTileBytes;
+        const char* Vt = KS ? v_slot0 : v_slot1;
         s16x4 lo[4 * kKC], hi[4 * kKC];
 #pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
@@ -287,13 +292,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, kAheadV, 0);
       }
       if (jj < nT) {
-        const char* Kt = Ks + KS * kTileBytes;
+        const char* Kt = KS ? k_slot1 : k_slot0;
         bf16x8 kf[8 * kKB];
 #pragma unroll
         for (int c = 0; c < 8; ++c)
 #pragma unroll
           for (int kb = 0; kb < kKB; ++kb)
             kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
+
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -393,39 +399,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     // Tile j's K and tile j-1's V stay in LDS for intervals 2j and 2j+1; the
     // slots of K(j-1) and V(j-2) are free from interval 2j on (their last
     // reader, group 1's GEMM(j-1), ran in interval 2j-1). Group 1 loads K(j+1)
-    // during its softmax phase of interval 2j, group 0 loads V(j) during its
-    // softmax phase of interval 2j+1; each waits for its loads at the end of
-    // that phase, before the barrier that publishes them, and both are in
-    // place for group 0's GEMM(j+1) in interval 2j+2.
+    // during its softmax phase of interval 2j and waits for it at the end of
+    // its GEMM phase of interval 2j+1; group 0 loads V(j) during its softmax
+    // phase of interval 2j+1 and waits for it at the end of that phase. Both
+    // waits come before the barrier that publishes the tiles, in place for
+    // group 0's GEMM(j+1) in interval 2j+2.
     const int nIntervals = 2 * nT + 2;
     for (int i = 0; i < nIntervals; i += 4) {
       const int j0 = i >> 1;
       if (group == 0) gemm(Int<0>{}, j0);
       else {
-        if (j0 + 1 < nT) dma_k(j0 + 1, 1);
+        if (j0 + 1 < nT) dma_k(j0 + 1, Int<1>{});
         softmax(j0 - 1);
-        __builtin_amdgcn_s_waitcnt(kWaitLoads);
       }
       phase_barrier();
       if (group == 0) {
-        if (j0 < nT) dma_v(j0, 0);
+        if (j0 < nT) dma_v(j0, Int<0>{});
         softmax(j0);
-        __builtin_amdgcn_s_waitcnt(kWaitLoads);
       } else gemm(Int<0>{}, j0);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
       phase_barrier();
       const int j1 = j0 + 1;
       if (group == 0) gemm(Int<1>{}, j1);
       else {
-        if (j1 + 1 < nT) dma_k(j1 + 1, 0);
+        if (j1 + 1 < nT) dma_k(j1 + 1, Int<0>{});
         softmax(j0);
-        __builtin_amdgcn_s_waitcnt(kWaitLoads);
       }
       phase_barrier();
       if (group == 0) {
-        if (j1 < nT) dma_v(j1, 1);
+        if (j1 < nT) dma_v(j1, Int<1>{});
         softmax(j1);
-        __builtin_amdgcn_s_waitcnt(kWaitLoads);
       } else gemm(Int<1>{}, j1);
+      __builtin_amdgcn_s_waitcnt(kWaitLoads);
       phase_barrier();
     }
 
@@ -458,7 +463,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       // chunk c of row r at chunk c ^ (r % 16), then stores whole 256-byte row
       // segments, 4 rows per instruction, instead of 16-byte pieces of 32 rows.
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-      char* const st = smem + wave * (32 * kRowBytes);
+      char* const st = ((wave >> 1) == 0 ? k_slot0 : (wave >> 1) == 1 ? k_slot1
+                        : (wave >> 1) == 2 ? v_slot0 : v_slot1) + (wave & 1) * (32 * kRowBytes);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
