@@ -38,8 +38,8 @@
 //    needed one interval later), group 0 the next V tile, awaited at the end
 //    of the softmax phase. The four slots are separate LDS arrays, so the
 //    compiler places no wait for a load in flight before the reads of
-//    another slot. Rows past k_len fall outside the
-//    buffer resource and read as zero. Each 16-byte chunk of a row is
+//    another slot. Rows past k_len fall outside the buffer resource and read
+//    as zero. Each 16-byte chunk of a row is
 //    XOR-swizzled so the MFMA operand reads are bank-conflict free; a load
 //    writes 16 bytes per lane at base + 16 lane, so each lane fetches the
 //    global chunk that belongs there.
@@ -299,7 +299,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int kb = 0; kb < kKB; ++kb)
             kf[c * kKB + kb] = lds_read16(Kt + ka[c] + kb * 32 * kRowBytes);
-
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
