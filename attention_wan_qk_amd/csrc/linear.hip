@@ -25,6 +25,8 @@
 //    buffers are reached through restrict pointers of an inlined step
 //    function, so the compiler can tell that the loads in flight do not write
 //    what the step's LDS reads read, and places no wait before those reads.
+//  * Inside a k-step the LDS operand reads run a few fragments ahead of the
+//    MFMAs that use them (scheduling groups), instead of all before the first.
 //  * Each 16-byte chunk c of tile row r is stored at chunk c ^ ((r / 2) % 8),
 //    so the 16 rows read together at one logical chunk by a quarter of a
 //    wave fall into 16 different 16-byte bank groups.
@@ -51,10 +53,14 @@ constexpr int kRowBytes = kBK * 2;       // 128
 constexpr int kTileBytes = kBM * kRowBytes;  // 32 KiB (x and W tiles are the same size)
 constexpr int kLoads = kTileBytes / 16 / kThreads;  // 1 KiB loads per wave per tile: 4
 constexpr int kGroupM = 4;               // token tiles per band
+constexpr int kReadAhead = 7;            // LDS fragment reads issued ahead of the MFMAs
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ int chunk_phys(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -165,20 +171,32 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
-  // MFMAs of k-step kk (32 of the stage's 64 K values).
+  // MFMAs of k-step kk (32 of the stage's 64 K values). The 12 fragments are
+  // read in the order the MFMAs first use them (W row block 0, the 8 x row
+  // blocks, W row blocks 1-3), kReadAhead of them before the first MFMA and
+  // then one after each MFMA, so that an MFMA waits only for its own operands
+  // (all 12 reads before the first MFMA made every k-step wait for the last).
   auto mma = [&](const lds_char* __restrict__ xc, const lds_char* __restrict__ wc, int kk) {
     const lds_char* wb = wc + wa;
     const lds_char* xb = xc + xa;
     bf16x8 wf[4], xf[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i] = lds_read16(wb + ch[kk] + i * 16 * kRowBytes);
+    wf[0] = lds_read16(wb + ch[kk]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) xf[j] = lds_read16(xb + ch[kk] + j * 16 * kRowBytes);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) wf[i] = lds_read16(wb + ch[kk] + i * 16 * kRowBytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReadAhead, 0);
+#pragma unroll
+    for (int r = 0; r < 12 - kReadAhead; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 32 - (12 - kReadAhead), 0);
   };
   dma(0, X0, W0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
