@@ -199,7 +199,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinearArgs a) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 32 - (12 - kReadAhead), 0);
   };
   dma(0, X0, W0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Wait for everything here, the kernel-argument scalar loads included: with
+  // one of them possibly in flight at the loop head (scalar loads complete out
+  // of order), the compiler's first operand wait of every k-step would be for
+  // all LDS reads, not just the first MFMA's.
+  __builtin_amdgcn_s_waitcnt(0);
   barrier();
 
   // Waves 0-3 issue a stage's loads before its first k-step, waves 4-7 before
