@@ -1,5 +1,5 @@
 // Measurement aids (libwanpeak.so): the sustained bf16 MFMA rate and the
-// streaming copy bandwidth of the chip, against which the library's kernels
+// streaming copy, read and write bandwidths of the chip, against which the library's kernels
 // are also quoted. Not part of the attention path.
 #include <stdint.h>
 
@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = WANPEAK_MFMA_THREADS;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;   // 16-byte vectors per thread: 16 KiB per workgroup
+static_assert(kCopyThreads * kCopyUnroll * 16 == WANPEAK_STREAM_BLOCK_BYTES, "stream block size");
 
 // Four independent accumulator chains per wave keep the MFMA pipe busy; two
 // workgroups per CU give each SIMD two waves.
@@ -57,6 +58,46 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(u32x4* __restrict__ 
                                   dst + i + u * kCopyThreads);
 }
 
+// Read-only stream: each thread folds its vectors into one word by XOR and
+// the workgroup's XOR goes to out[blockIdx.x] (one 4-byte store per 16 KiB
+// read), so the loads cannot be removed and the result can be checked.
+__global__ __launch_bounds__(kCopyThreads) void read_kernel(uint32_t* __restrict__ out,
+                                                            const u32x4* __restrict__ src,
+                                                            size_t n) {
+  __shared__ uint32_t part[kCopyThreads / 64];
+  const size_t base = (size_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const size_t i = base + (size_t)u * kCopyThreads;
+    if (i < n) {
+      const u32x4 v = __builtin_nontemporal_load(src + i);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kCopyThreads / 64; ++w) r ^= part[w];
+    out[blockIdx.x] = r;
+  }
+}
+
+// Write-only stream: every 4-byte word of dst[0, n) set to `value`.
+__global__ __launch_bounds__(kCopyThreads) void fill_kernel(u32x4* __restrict__ dst, size_t n,
+                                                            uint32_t value) {
+  const size_t base = (size_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x;
+  const u32x4 v = {value, value, value, value};
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const size_t i = base + (size_t)u * kCopyThreads;
+    if (i < n) __builtin_nontemporal_store(v, dst + i);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +124,32 @@ int wanpeak_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (blocks > 0x7fffffffu) return 1;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
                      static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int wanpeak_read(uint32_t* out, const void* src, size_t bytes, hipStream_t stream) {
+  if (!out || !src || (bytes & 15u)) return 1;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return 1;
+  if (bytes == 0) return 0;
+  const size_t n = bytes / 16;
+  const size_t blocks = (bytes + WANPEAK_STREAM_BLOCK_BYTES - 1) / WANPEAK_STREAM_BLOCK_BYTES;
+  if (blocks > 0x7fffffffu) return 1;
+  const uintptr_t o = reinterpret_cast<uintptr_t>(out), s = reinterpret_cast<uintptr_t>(src);
+  if (o < s + bytes && s < o + blocks * 4) return 1;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream, out,
+                     static_cast<const u32x4*>(src), n);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int wanpeak_fill(void* dst, size_t bytes, uint32_t value, hipStream_t stream) {
+  if (!dst || (bytes & 15u) || (reinterpret_cast<uintptr_t>(dst) & 15u)) return 1;
+  if (bytes == 0) return 0;
+  const size_t n = bytes / 16;
+  const size_t blocks = (bytes + WANPEAK_STREAM_BLOCK_BYTES - 1) / WANPEAK_STREAM_BLOCK_BYTES;
+  if (blocks > 0x7fffffffu) return 1;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
+                     static_cast<u32x4*>(dst), n, value);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

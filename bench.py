@@ -307,7 +307,8 @@ def measured_peaks(memory_gbs):
     steps: a bf16 MFMA loop (512 workgroups of 4 waves, 4 independent
     accumulator chains per wave, random operands, ~0.3 s per launch, so that
     the chip reaches the clock it holds under full MFMA load; fastest of 3
-    launches) and a 2 GiB nontemporal device copy (fastest of 10 launches).
+    launches) and a 2 GiB nontemporal device copy, then the same bytes read
+    alone and written alone (fastest of 10 launches each).
     Returns (MFMA TFLOP/s, copy GB/s); the memory calls' rates are printed
     against the copy on stderr."""
     import torch
@@ -338,11 +339,25 @@ def measured_peaks(memory_gbs):
         ev[i + 1].record()
     torch.cuda.synchronize()
     copy_gbs = 2 * n / (min(ev[i].elapsed_time(ev[i + 1]) for i in range(10)) * 1e-3) / 1e9
-    del src, dst
+    # the same 2 GiB read alone and written alone
+    words = torch.empty(peaks.read_blocks(n), dtype=torch.int32, device=dev)
+    rates = []
+    for run in (lambda: peaks.read(words, src), lambda: peaks.fill(dst, 0x3F803F80)):
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        ev[0].record()
+        for i in range(10):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        rates.append(n / (min(ev[i].elapsed_time(ev[i + 1]) for i in range(10)) * 1e-3) / 1e9)
+    read_gbs, write_gbs = rates
+    del src, dst, words
     print(json.dumps({"measured_peaks": {
         "mfma_bf16_loop_tflops": round(mfma_tf, 1), "mfma_loop_ms": [round(m, 2) for m in ms],
         "mfma_loop_frac_of_spec": round(mfma_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         "copy_gbs": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+        "read_gbs": round(read_gbs, 1), "write_gbs": round(write_gbs, 1),
         "memory_calls_frac_of_copy": {k: round(v / copy_gbs, 4) for k, v in memory_gbs.items()},
     }}), file=sys.stderr, flush=True)
     return mfma_tf, copy_gbs

@@ -9,7 +9,11 @@
  *                           v_mfma_f32_32x32x16_bf16 on fixed operands
  *                           (2 * 32 * 32 * 16 = 32768 FLOP each);
  *   wanpeak_copy            a streaming device-to-device copy with 16-byte
- *                           nontemporal loads and stores.
+ *                           nontemporal loads and stores;
+ *   wanpeak_read            the same loads alone (reads only);
+ *   wanpeak_fill            the same stores alone (writes only).
+ * A copy reads and writes the same number of bytes, as the row calls of the
+ * library do; the read-only and write-only rates bound it from either side.
  *
  * Library libwanpeak.so, built beside libwanattn.so. Pointers are caller-owned
  * device memory; nothing is allocated or synchronised; work goes on `stream`
@@ -21,6 +25,7 @@
 #define WANPEAK_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -30,6 +35,10 @@ extern "C" {
 
 /* Threads per workgroup of wanpeak_mfma_bf16_loop (4 waves). */
 #define WANPEAK_MFMA_THREADS 256
+
+/* Bytes of the source that one workgroup of wanpeak_read (and of
+   wanpeak_fill) covers: 256 threads x 4 vectors of 16 bytes. */
+#define WANPEAK_STREAM_BLOCK_BYTES 16384
 
 /*
  * Runs `blocks` workgroups of WANPEAK_MFMA_THREADS threads; each wave does
@@ -52,6 +61,23 @@ int wanpeak_mfma_bf16_loop(const void* operands, float* out, int blocks, int ite
  * bytes = 0 launches nothing. The launch moves 2 * bytes through HBM.
  */
 int wanpeak_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/*
+ * Reads src[0, bytes) once. out[i] (ceil(bytes / WANPEAK_STREAM_BLOCK_BYTES)
+ * words, 4-byte aligned, not overlapping src) receives the XOR of all 4-byte
+ * words of block i of the source: the check that every byte was read. bytes
+ * must be a multiple of 16 and src 16-byte aligned, else 1 (invalid); bytes
+ * = 0 launches nothing. The launch moves `bytes` through HBM (plus 4 bytes per
+ * block written).
+ */
+int wanpeak_read(uint32_t* out, const void* src, size_t bytes, hipStream_t stream);
+
+/*
+ * Sets every 4-byte word of dst[0, bytes) to `value`. bytes must be a multiple
+ * of 16 and dst 16-byte aligned, else 1 (invalid); bytes = 0 launches nothing.
+ * The launch moves `bytes` through HBM.
+ */
+int wanpeak_fill(void* dst, size_t bytes, uint32_t value, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -327,7 +327,8 @@ def test_peak_library_exports_and_host_checks(P):
     from attention_wan_qk_amd import peaks
     declared = sorted(set(re.findall(r"^\s*int\s+(wanpeak_\w+)\s*\(", open(PEAK_HEADER).read(),
                                      re.M)))
-    assert declared == ["wanpeak_copy", "wanpeak_mfma_bf16_loop"]
+    assert declared == ["wanpeak_copy", "wanpeak_fill", "wanpeak_mfma_bf16_loop",
+                        "wanpeak_read"]
     out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert set(re.findall(r"\bT (wanpeak_\w+)", out)) == set(declared)
@@ -345,4 +346,19 @@ def test_peak_library_exports_and_host_checks(P):
     assert cp(A + 8, A + MB, 16, None) == 1          # misaligned
     assert cp(A, A + 16, 32, None) == 1              # overlapping ranges
     assert cp(A, A + MB, 0, None) == 0               # nothing to do: no launch
+    rd = P.wanpeak_read
+    assert rd(None, A, 16, None) == 1
+    assert rd(A, None, 16, None) == 1
+    assert rd(A + MB, A, 24, None) == 1              # not a multiple of 16
+    assert rd(A + MB, A + 8, 16, None) == 1          # source misaligned
+    assert rd(A + MB + 2, A, 16, None) == 1          # out not 4-byte aligned
+    assert rd(A + 16, A, 1 << 20, None) == 1         # out inside the source
+    assert rd(A + MB, A, 0, None) == 0               # nothing to do: no launch
+    fl = P.wanpeak_fill
+    assert fl(None, 16, 0, None) == 1
+    assert fl(A, 24, 0, None) == 1                   # not a multiple of 16
+    assert fl(A + 8, 16, 0, None) == 1               # misaligned
+    assert fl(A, 0, 0, None) == 0                    # nothing to do: no launch
+    assert peaks.read_blocks(1) == 1 and peaks.read_blocks(16384) == 1
+    assert peaks.read_blocks(16385) == 2
     assert peaks.mfma_loop_flop(512, 10) == 512 * 4 * 10 * 4 * 32768

@@ -1,10 +1,12 @@
 """The measurement aids of libwanpeak.so on the GPU: the MFMA loop's FLOP
 accounting (all-ones operands make every accumulator element 16 per MFMA,
-so a thread's sum is 4 chains x 16 elements x 16 x iters) and the copy
-(bytes identical, including a ragged last workgroup)."""
+so a thread's sum is 4 chains x 16 elements x 16 x iters), the copy (bytes
+identical, including a ragged last workgroup), the read (each 16 KiB block's
+XOR of 4-byte words, computed again on the CPU) and the fill."""
 
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -44,3 +46,29 @@ def test_copy(nbytes):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nbytes], src)
     assert not dst[nbytes:].any()
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1024, 16 * 1024 + 48, (3 << 20) + 80])
+def test_read_xor(nbytes):
+    print(f"[case] read {nbytes} bytes", flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(nbytes + 1)
+    src = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8)
+    nb = peaks.read_blocks(nbytes)
+    out = torch.full((nb,), -1, dtype=torch.int32, device=DEV)
+    peaks.read(out, src.to(DEV))
+    torch.cuda.synchronize()
+    words = src.view(torch.int32).numpy()
+    per = peaks.STREAM_BLOCK_BYTES // 4
+    want = [int(np.bitwise_xor.reduce(words[i * per:(i + 1) * per])) for i in range(nb)]
+    assert out.cpu().tolist() == want
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1024 + 48, (1 << 20) + 48])
+def test_fill(nbytes):
+    print(f"[case] fill {nbytes} bytes", flush=True)
+    buf = torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)
+    peaks.fill(buf[:nbytes], 0x3F803F80)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:nbytes].view(torch.int32) == 0x3F803F80)
+    assert not buf[nbytes:].any()
